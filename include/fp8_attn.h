@@ -1,0 +1,170 @@
+/*
+ * fp8_attn.h -- C ABI of the MI355X (gfx950) causal FP8 (OCP E4M3FN) attention
+ * forward studied on the "attention-numerics" pages (mottopanikeiku.github.io)
+ * and in the "P-Cast Precisie in FP8 Attention" summary (gist.science).
+ *
+ * General conventions
+ *   - Every pointer argument named as "device" is device memory owned by the
+ *     caller; its lifetime must cover the work enqueued on `stream`.  The
+ *     library allocates and frees nothing; scratch memory comes from the
+ *     caller through a workspace argument sized by the *_workspace_bytes call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call validates its arguments on the host first; a failed check
+ *     returns a negative status and enqueues nothing.  No call synchronises.
+ *   - Layout: operands are [batch, head, token, channel] with the channel axis
+ *     contiguous; the other axes use the element strides in fp8a_shape (a
+ *     stride triple of zeros means dense).  Grouped-query attention: query
+ *     head h reads KV head h / (hq / hkv).
+ *   - Quantised operands use a padded token count Np = fp8_attn_padded_seqlen(N)
+ *     (a multiple of 128); rows/columns past N hold code 0.
+ *   - Thread safety: no global mutable state; concurrent calls on different
+ *     streams with disjoint outputs are independent.
+ */
+#ifndef FP8_ATTN_H
+#define FP8_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8A_OK = 0,
+  FP8A_ERR_NULL = -1,        /* a required pointer is NULL */
+  FP8A_ERR_SHAPE = -2,       /* sizes or strides outside what the kernels support */
+  FP8A_ERR_UNSUPPORTED = -3, /* a valid request this library does not implement */
+  FP8A_ERR_PARAM = -4,       /* a scalar parameter out of range */
+  FP8A_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  FP8A_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+} fp8a_status;
+
+typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3 } fp8a_dtype;
+
+/* Prologue flags.  ROTATE: fixed random-sign Hadamard on Q and K, never V
+ * (attention-numerics study page, "See the vectors and the arithmetic").
+ * CENTER: subtract the full-sequence mean key before rotation (project page,
+ * second section; study page, same panel). */
+#define FP8A_ROTATE_QK 1u
+#define FP8A_CENTER_K 2u
+
+typedef struct {
+  int32_t batch;     /* B >= 1 */
+  int32_t hq;        /* query heads >= 1 */
+  int32_t hkv;       /* KV heads >= 1, hq % hkv == 0 */
+  int32_t seqlen;    /* N >= 1 (token count of every head) */
+  int32_t head_dim;  /* d: 64 or 128 */
+  int64_t q_stride[3], k_stride[3], v_stride[3]; /* element strides of (batch, head, token) */
+} fp8a_shape;
+
+/* Np: the token count padded to a multiple of 128. */
+int32_t fp8_attn_padded_seqlen(int32_t seqlen);
+
+/* Workspace needed by fp8_attn_prepare for this shape and flags (bytes). */
+size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* shape, uint32_t flags);
+
+/*
+ * fp8_attn_prepare -- quantisation prologue.
+ *
+ * Computes, per (batch, head) over the full sequence (project page, second
+ * section: independent Q/K/V scales over the full sequence for each batch and
+ * head):
+ *   1. if CENTER: mu[b,g,:] = mean over all N tokens of K[b,g,:,:], in binary64
+ *      (chunks of 64 tokens summed in order, chunk sums added in a pairwise
+ *      tree), rounded to binary32; K' = K - mu.
+ *   2. if ROTATE: for Q and K' (never V) each row is multiplied by
+ *      rot_signs and passed through the unnormalised Sylvester Walsh-Hadamard
+ *      transform (stages h = 1, 2, ..., d/2) in binary32.
+ *   3. A = max |x| per head of the transformed Q, K and of raw V; the scale
+ *      448/A quantises, the descale A/448 (times RN32(1/sqrt(d)) for the
+ *      rotated Q and K) is written out.  A = 0 gives scale and descale 1.
+ *   4. codes = E4M3FN(x * 448/A), round-to-nearest-even, saturating at +-448
+ *      (study page, "See the vectors and the arithmetic").
+ *
+ * Arguments
+ *   in_dtype   FP8A_F32 or FP8A_BF16: element type of q, k, v (device).
+ *   q, k, v    device, [B,hq,N,d] / [B,hkv,N,d] with the shape's strides.
+ *   rot_signs  device int8[d] of +-1; required with ROTATE, else ignored.
+ *   q8         device out, [B,hq,Np,d] E4M3FN codes.
+ *   k8         device out, [B,hkv,Np,d] codes.
+ *   v8t        device out, [B,hkv,d,Np] codes (V transposed: token axis contiguous).
+ *   q_desc     device out, float[B*hq];  k_desc, v_desc: float[B*hkv].
+ *   k_mean     device out, float[B*hkv*d]; written when CENTER (may be NULL).
+ *   status_word device out, int32 (may be NULL): bit 0 is set when any input
+ *              element was NaN or infinite; the codes are then unspecified.
+ *   workspace  device scratch of fp8_attn_prepare_workspace_bytes().
+ */
+int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
+                     const void* q, const void* k, const void* v, uint32_t flags,
+                     const int8_t* rot_signs,
+                     uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                     float* q_desc, float* k_desc, float* v_desc, float* k_mean,
+                     int32_t* status_word, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_attn_fwd -- attention main loop and epilogue.
+ *
+ * For every query row i, the KV blocks [jB, (j+1)B) holding a visible key
+ * (j <= i when causal) are visited in forward (0 -> N) or reverse (N -> 0)
+ * order (P-Cast summary, Probleemstelling, item 1).  With E4M3 operands the
+ * score is the FP8 matrix-core dot product of the codes; c = (q_desc*k_desc)
+ * * RN32(softmax_scale*log2 e); per block the running max m (over raw scores)
+ * is updated, x = fma(s, c, -RN32(m*c)), p = 2^x (binary32, correctly
+ * rounded wherever it decides a code), l <- l*alpha + sum p, and
+ * P~ = E4M3(S*p) enters the FP8 product with V (P-Cast summary, item 2: the
+ * static scale S is applied before the E4M3 cast and divided out in the
+ * epilogue): out = acc * (v_desc / (S*l)).
+ *
+ * Arguments
+ *   qkv_dtype  FP8A_E4M3: q = q8 [B,hq,Np,d], k = k8 [B,hkv,Np,d], v = v8t
+ *              [B,hkv,d,Np] as written by fp8_attn_prepare, descales required.
+ *              FP8A_F32: dense binary32 q/k/v [B,h,N,d], only P is cast
+ *              ("kernel-faithful" simulation of the P-Cast summary, Bijdragen
+ *              item 4); scores are an ordered binary32 fma chain over the
+ *              channels; descales must be NULL.
+ *   softmax_scale  > 0, usually 1/sqrt(d).
+ *   p_scale    S: a power of two in [1, 256] or 448.
+ *   kv_order   0 forward, 1 reverse.   block_n: 64 or 128.   causal: 0 or 1.
+ *   out        device out, float [B,hq,N,d].
+ *   lse        device out, float [B,hq,N] natural-log sum-exp of the scaled
+ *              logits (may be NULL).
+ *   p_dump     device out, uint8 [B,hq,N,N] P~ codes (may be NULL): every key of
+ *              every visited block is written (0 for masked keys); keys of
+ *              unvisited blocks are left untouched, so zero it first.
+ *   row_zeros  device out, uint32 [B,hq,N] (may be NULL): number of visible
+ *              keys j >= k_sink whose P~ code is 0.
+ */
+int fp8_attn_fwd(const fp8a_shape* shape, fp8a_dtype qkv_dtype,
+                 const void* q, const void* k, const void* v,
+                 const float* q_desc, const float* k_desc, const float* v_desc,
+                 float softmax_scale, float p_scale, int32_t kv_order, int32_t block_n, int32_t causal,
+                 float* out, float* lse, uint8_t* p_dump, uint32_t* row_zeros, int32_t k_sink,
+                 void* stream);
+
+/* Workspace needed by fp8_attn_head_error (bytes). */
+size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* shape, int64_t nrows);
+
+/*
+ * fp8_attn_head_error -- relative Frobenius output error per (batch, head):
+ * rel_err[b*hq+h] = ||O - R||_F / ||R||_F over the head's rows, sums in
+ * binary64 (project page: each head's output against ideal causal FP64
+ * attention; study page, "What do these scores mean?").
+ *
+ *   out        device, float [B,hq,N,d] (as written by fp8_attn_fwd).
+ *   ref        device, [B,hq,nrows,d] of ref_dtype FP8A_F32 or FP8A_F64.
+ *   rows       device int32[nrows] of query positions in [0, N), or NULL for
+ *              all rows (then nrows must equal N).
+ *   rel_err    device out, double [B*hq].
+ */
+int fp8_attn_head_error(const fp8a_shape* shape, const float* out, const void* ref, fp8a_dtype ref_dtype,
+                        const int32_t* rows, int64_t nrows, double* rel_err,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* fp8_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8_ATTN_H */

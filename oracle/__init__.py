@@ -91,9 +91,13 @@ def _p(a: np.ndarray | None, ctype):
 
 
 def _threads(n: int | None) -> int:
+    """Worker threads: ORACLE_THREADS if set, else the usable cores (at most 16)."""
     if n is not None:
         return int(n)
-    return int(os.environ.get("ORACLE_THREADS", "0"))
+    env = os.environ.get("ORACLE_THREADS")
+    if env:
+        return int(env)
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _check(rc: int, what: str):

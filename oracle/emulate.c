@@ -146,8 +146,8 @@ static inline int64_t rn32_units(int64_t v) {
  * precision: each product magnitude is truncated (toward zero) to a multiple
  * of 2^(R-13), R being the largest scale exponent E_a + E_b among the
  * non-zero products of the group; the truncated products are then added
- * exactly. */
-static int64_t group8_units(const uint8_t* a, const uint8_t* b, int k0) {
+ * exactly.  *rmax receives max(*rmax, R). */
+static int64_t group8_units(const uint8_t* a, const uint8_t* b, int k0, int* rmax) {
   int sg[8], sp[8], ep[8], R = -1000;
   for (int i = 0; i < 8; ++i) {
     int s1, m1, e1, s2, m2, e2;
@@ -156,6 +156,7 @@ static int64_t group8_units(const uint8_t* a, const uint8_t* b, int k0) {
     sg[i] = s1 * s2; sp[i] = m1 * m2; ep[i] = e1 + e2;
     if (sp[i] != 0 && ep[i] > R) R = ep[i];
   }
+  if (R > *rmax) *rmax = R;
   int64_t sum = 0;
   if (R == -1000) return 0;
   int lsb = R - 13 + UNIT_SHIFT; /* truncation quantum, in units (>= 0 because R >= -12) */
@@ -166,6 +167,15 @@ static int64_t group8_units(const uint8_t* a, const uint8_t* b, int k0) {
     sum += sg[i] * mag;
   }
   return sum;
+}
+
+/* Largest multiple of 2^(anchor-24) not above v (two's-complement
+ * truncation); v is in units of 2^-25, so quanta finer than one unit leave it
+ * unchanged. */
+static inline int64_t floor_window(int64_t v, int anchor) {
+  int s = anchor - 24 + UNIT_SHIFT;
+  if (s <= 0) return v;
+  return v & ~(((int64_t)1 << s) - 1);
 }
 
 float orc_fp8_dot128(const uint8_t* a, const uint8_t* b, int mode) {
@@ -182,13 +192,20 @@ float orc_fp8_dot128(const uint8_t* a, const uint8_t* b, int mode) {
   /* The 128 products are taken as eight passes of sixteen (two groups of
    * eight each): passes 0, 2, 4, 6 cover k = 0-15, 32-47, 64-79, 96-111 and
    * come first, then passes 1, 3, 5, 7 (k = 16-31, 48-63, 80-95, 112-127).
-   * Each pass adds its two group sums to the running binary32 value exactly
-   * and rounds once to nearest-even. */
+   * In each pass the two group sums are added and the result truncated
+   * (floor) to a multiple of 2^(R-24), R the largest product scale exponent
+   * of the pass; that is added to the running binary32 value, truncated the
+   * same way, and rounded to binary32 (nearest-even).  A pass whose products
+   * are all zero leaves the running value unchanged. */
   static const int pass_order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
   int64_t acc = 0;
   for (int t = 0; t < 8; ++t) {
-    int p = pass_order[t];
-    acc = rn32_units(acc + group8_units(a, b, 16 * p) + group8_units(a, b, 16 * p + 8));
+    int p = pass_order[t], R = -1000;
+    int64_t ga = group8_units(a, b, 16 * p, &R);
+    int64_t gb = group8_units(a, b, 16 * p + 8, &R);
+    if (R == -1000) continue;
+    int64_t part = floor_window(ga + gb, R);
+    acc = rn32_units(floor_window(acc + part, R));
   }
   return (float)ldexp((double)acc, -UNIT_SHIFT);
 }

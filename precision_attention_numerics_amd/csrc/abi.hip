@@ -1,0 +1,222 @@
+// extern "C" entry points of libfp8attn: host-side validation, workspace
+// layout and kernel launches.  See include/fp8_attn.h for the contract.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/fp8_attn.h"
+#include "attn.hpp"
+#include "prepare.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const fp8a_shape* s) {
+  if (!s) return FP8A_ERR_NULL;
+  if (s->batch < 1 || s->hq < 1 || s->hkv < 1 || s->seqlen < 1) return FP8A_ERR_SHAPE;
+  if (s->hq % s->hkv != 0) return FP8A_ERR_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return FP8A_ERR_SHAPE;
+  if (s->seqlen > (1 << 30)) return FP8A_ERR_SHAPE;
+  return FP8A_OK;
+}
+
+// Resolves a stride triple (zeros = dense) and checks the 16-byte row
+// alignment the vector loads need.
+int resolve_strides(const int64_t in[3], int32_t H, const fp8a_shape* s, int64_t out[3]) {
+  const int64_t N = s->seqlen, d = s->head_dim;
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    out[0] = H * N * d; out[1] = N * d; out[2] = d;
+    return FP8A_OK;
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (in[i] < 0 || in[i] % 8 != 0) return FP8A_ERR_SHAPE;
+    out[i] = in[i];
+  }
+  if (out[2] < d) return FP8A_ERR_SHAPE;
+  return FP8A_OK;
+}
+
+int32_t np2_chunks(int32_t N) {
+  const int32_t nchunk = (N + 63) / 64;
+  int32_t np2 = 1;
+  while (np2 < nchunk) np2 <<= 1;
+  return np2;
+}
+
+int32_t err_chunks(int32_t BH, int64_t nrows) {
+  int64_t n = (2048 + BH - 1) / BH;
+  if (n > nrows) n = nrows;
+  if (n < 1) n = 1;
+  return static_cast<int32_t>(n);
+}
+
+// exp2 patch table: binary32 patterns of x where v_exp_f32 would flip the
+// E4M3 code of S * 2^x (see the attention kernel).
+bool p_scale_setup(float S, bool* pow2, float* inv_S, uint32_t* bad0, uint32_t* bad1) {
+  if (S == 448.0f) {
+    *pow2 = false; *inv_S = 0.0f; *bad0 = 0xbf5a689au; *bad1 = 0xbfed344du;
+    return true;
+  }
+  for (int k = 0; k <= 8; ++k) {
+    if (S == ldexpf(1.0f, k)) {
+      *pow2 = true; *inv_S = ldexpf(1.0f, -k); *bad0 = 0xbd3b9cb2u; *bad1 = 0xbef3efb2u;
+      return true;
+    }
+  }
+  return false;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8A_OK : FP8A_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8_attn_padded_seqlen(int32_t seqlen) {
+  if (seqlen < 1) return 0;
+  return (seqlen + 127) / 128 * 128;
+}
+
+size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* s, uint32_t flags) {
+  if (check_shape(s) != FP8A_OK) return 0;
+  const size_t B = s->batch, hq = s->hq, hkv = s->hkv, d = s->head_dim;
+  size_t bytes = align_up(B * (hq + 2 * hkv) * sizeof(uint32_t));
+  if (flags & FP8A_CENTER_K) {
+    bytes += align_up(B * hkv * static_cast<size_t>(np2_chunks(s->seqlen)) * d * sizeof(double));
+    bytes += align_up(B * hkv * d * sizeof(float));
+  }
+  return bytes;
+}
+
+int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, const void* k, const void* v,
+                     uint32_t flags, const int8_t* rot_signs, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                     float* q_desc, float* k_desc, float* v_desc, float* k_mean, int32_t* status_word,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (in_dtype != FP8A_F32 && in_dtype != FP8A_BF16) return FP8A_ERR_UNSUPPORTED;
+  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K)) return FP8A_ERR_PARAM;
+  if (!q || !k || !v || !q8 || !k8 || !v8t || !q_desc || !k_desc || !v_desc) return FP8A_ERR_NULL;
+  if ((flags & FP8A_ROTATE_QK) && !rot_signs) return FP8A_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
+    return FP8A_ERR_SHAPE;
+  const size_t need = fp8_attn_prepare_workspace_bytes(s, flags);
+  if (!workspace || workspace_bytes < need) return FP8A_ERR_WORKSPACE;
+  fp8a::PrepareArgs a;
+  memset(&a, 0, sizeof a);
+  if ((rc = resolve_strides(s->q_stride, s->hq, s, a.qs))) return rc;
+  if ((rc = resolve_strides(s->k_stride, s->hkv, s, a.ks))) return rc;
+  if ((rc = resolve_strides(s->v_stride, s->hkv, s, a.vs))) return rc;
+  a.B = s->batch; a.hq = s->hq; a.hkv = s->hkv; a.N = s->seqlen; a.Np = fp8_attn_padded_seqlen(s->seqlen);
+  a.D = s->head_dim;
+  a.bf16 = in_dtype == FP8A_BF16;
+  a.rotate = (flags & FP8A_ROTATE_QK) != 0;
+  a.center = (flags & FP8A_CENTER_K) != 0;
+  a.q = q; a.k = k; a.v = v;
+  a.signs = rot_signs;
+  a.cd = static_cast<float>(1.0 / sqrt(static_cast<double>(s->head_dim)));
+  a.q8 = q8; a.k8 = k8; a.v8t = v8t;
+  a.q_desc = q_desc; a.k_desc = k_desc; a.v_desc = v_desc;
+  a.status = status_word;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.amax = reinterpret_cast<uint32_t*>(ws);
+  ws += align_up(static_cast<size_t>(a.B) * (a.hq + 2 * a.hkv) * sizeof(uint32_t));
+  a.np2 = np2_chunks(a.N);
+  if (a.center) {
+    a.mean_part = reinterpret_cast<double*>(ws);
+    ws += align_up(static_cast<size_t>(a.B) * a.hkv * a.np2 * a.D * sizeof(double));
+    a.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws);
+  }
+  return hip_status(fp8a::launch_prepare(a, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                 const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
+                 float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out, float* lse,
+                 uint8_t* p_dump, uint32_t* row_zeros, int32_t k_sink, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32) return FP8A_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return FP8A_ERR_NULL;
+  if (qkv_dtype == FP8A_E4M3 && (!q_desc || !k_desc || !v_desc)) return FP8A_ERR_NULL;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FP8A_ERR_PARAM;
+  if (!(p_scale > 0.0f) || !(p_scale <= 448.0f)) return FP8A_ERR_PARAM;
+  if (kv_order != 0 && kv_order != 1) return FP8A_ERR_PARAM;
+  if (block_n != 64 && block_n != 128) return FP8A_ERR_PARAM;
+  if (causal != 0 && causal != 1) return FP8A_ERR_PARAM;
+  if (k_sink < 0) return FP8A_ERR_PARAM;
+  bool pow2 = false;
+  float inv_S = 0.0f;
+  uint32_t bad0 = 0, bad1 = 0;
+  if (!p_scale_setup(p_scale, &pow2, &inv_S, &bad0, &bad1)) return FP8A_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FP8A_ERR_SHAPE;
+  const float ls2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (qkv_dtype == FP8A_F32) {
+    fp8a::PcastParams p;
+    memset(&p, 0, sizeof p);
+    p.q = static_cast<const float*>(q); p.k = static_cast<const float*>(k); p.v = static_cast<const float*>(v);
+    p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_zeros = row_zeros;
+    p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.block_n = block_n;
+    p.kv_order = kv_order; p.causal = causal; p.k_sink = k_sink;
+    p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
+    return hip_status(fp8a::launch_pcast_f32(p, s->head_dim, pow2, st));
+  }
+  fp8a::FwdParams p;
+  memset(&p, 0, sizeof p);
+  p.q8 = static_cast<const uint8_t*>(q); p.k8 = static_cast<const uint8_t*>(k); p.v8t = static_cast<const uint8_t*>(v);
+  p.q_desc = q_desc; p.k_desc = k_desc; p.v_desc = v_desc;
+  p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_zeros = row_zeros;
+  p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.Np = fp8_attn_padded_seqlen(s->seqlen);
+  p.n_qtiles = p.Np / 128; p.kv_order = kv_order; p.k_sink = k_sink;
+  p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
+  const bool dump = p_dump != nullptr || row_zeros != nullptr;
+  return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));
+}
+
+size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* s, int64_t nrows) {
+  if (check_shape(s) != FP8A_OK || nrows < 1) return 0;
+  const int32_t BH = s->batch * s->hq;
+  return align_up(static_cast<size_t>(BH) * err_chunks(BH, nrows) * 2 * sizeof(double));
+}
+
+int fp8_attn_head_error(const fp8a_shape* s, const float* out, const void* ref, fp8a_dtype ref_dtype,
+                        const int32_t* rows, int64_t nrows, double* rel_err, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!out || !ref || !rel_err) return FP8A_ERR_NULL;
+  if (ref_dtype != FP8A_F32 && ref_dtype != FP8A_F64) return FP8A_ERR_UNSUPPORTED;
+  if (nrows < 1 || (!rows && nrows != s->seqlen)) return FP8A_ERR_SHAPE;
+  const size_t need = fp8_attn_head_error_workspace_bytes(s, nrows);
+  if (!workspace || workspace_bytes < need) return FP8A_ERR_WORKSPACE;
+  fp8a::HeadErrParams p;
+  memset(&p, 0, sizeof p);
+  p.out = out; p.ref = ref; p.rows = rows; p.rel_err = rel_err;
+  p.part = static_cast<double*>(workspace);
+  p.nrows = nrows; p.BH = s->batch * s->hq; p.N = s->seqlen; p.D = s->head_dim;
+  p.nchunk = err_chunks(p.BH, nrows);
+  p.ref_f64 = ref_dtype == FP8A_F64;
+  return hip_status(fp8a::launch_head_error(p, static_cast<hipStream_t>(stream)));
+}
+
+const char* fp8_attn_strerror(int status) {
+  switch (status) {
+    case FP8A_OK: return "ok";
+    case FP8A_ERR_NULL: return "a required pointer is NULL";
+    case FP8A_ERR_SHAPE: return "sizes, strides or alignment not supported";
+    case FP8A_ERR_UNSUPPORTED: return "request not implemented (dtype or p_scale)";
+    case FP8A_ERR_PARAM: return "scalar parameter out of range";
+    case FP8A_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8A_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,324 @@
+// Quantisation prologue kernels for gfx950: mean key, per-head amax, fused
+// centre + random-sign Walsh-Hadamard + E4M3 quantise, and V quantise into the
+// transposed layout the attention core reads.
+//
+// What is computed follows the attention-numerics project page (second
+// section: independent Q/K/V scales over the full sequence for each batch and
+// head; the same Hadamard on Q and K, never V; mean-key subtraction) and the
+// study page ("See the vectors and the arithmetic": one maximum-based scale,
+// E4M3FN with round-to-nearest-even and saturation at +-448).
+//
+// All of these kernels are HBM-bound streaming passes.  Rows are handled by
+// groups of D/8 consecutive lanes holding 8 channels each, so a wave reads
+// whole rows with 16-byte loads; the Hadamard stages within a lane run in
+// registers and the cross-lane stages use lane shuffles.  Every binary32
+// operation is the one the stage order prescribes, so the codes are bit-exact
+// reproducible.
+#include "device_common.hpp"
+#include "prepare.hpp"
+
+namespace fp8a {
+
+template <typename IT>
+__device__ __forceinline__ void load8(const IT* p, float x[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float x[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float x[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t value, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// Partial sums of the mean key: one block per (chunk of 64 tokens, KV head),
+// one thread per channel; tokens are added in increasing order in binary64
+// starting from +0.0.  Chunks in [nchunk, np2) are the tree's zero padding.
+template <typename IT>
+__global__ void k_kmean_partial(const IT* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
+                                int32_t hkv, int32_t N, int32_t D, int32_t np2, double* __restrict__ part) {
+  const int32_t t = blockIdx.x, bg = blockIdx.y, c = threadIdx.x;
+  if (c >= D) return;
+  const int32_t b = bg / hkv, g = bg % hkv;
+  double s = 0.0;
+  const int32_t n0 = t * 64;
+  const int32_t n1 = min(n0 + 64, N);
+  const IT* base = k + b * sb + g * sh + c;
+  for (int32_t n = n0; n < n1; ++n) {
+    float x;
+    if constexpr (sizeof(IT) == 2) x = bf16_to_f32(base[static_cast<int64_t>(n) * sn]);
+    else x = base[static_cast<int64_t>(n) * sn];
+    s += static_cast<double>(x);
+  }
+  part[(static_cast<int64_t>(bg) * np2 + t) * D + c] = s;
+}
+
+// Pairwise tree over the chunk partials (in place), then one binary64 division
+// by N and rounding to binary32.
+__global__ void k_kmean_final(double* __restrict__ part, int32_t np2, int32_t N, int32_t D, float* __restrict__ mu) {
+  const int32_t bg = blockIdx.x, c = threadIdx.x;
+  if (c >= D) return;
+  double* col = part + static_cast<int64_t>(bg) * np2 * D + c;
+  for (int32_t w = np2; w > 1; w >>= 1)
+    for (int32_t t = 0; t < w / 2; ++t) col[static_cast<int64_t>(t) * D] = col[static_cast<int64_t>(2 * t) * D] + col[static_cast<int64_t>(2 * t + 1) * D];
+  mu[static_cast<int64_t>(bg) * D + c] = static_cast<float>(col[0] / static_cast<double>(N));
+}
+
+// One row (D channels) held by D/8 lanes, 8 channels per lane: optional
+// centring, sign flip and unnormalised Sylvester Walsh-Hadamard transform in
+// the stage order h = 1, 2, ..., D/2.
+template <int D, bool ROT, bool CENTER>
+__device__ __forceinline__ void transform_row(float x[8], int li, const float* __restrict__ mu,
+                                              const int8_t* __restrict__ signs) {
+  if constexpr (CENTER) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] - mu[8 * li + e];
+  }
+  if constexpr (ROT) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * static_cast<float>(signs[8 * li + e]);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((i & h) == 0) {
+          const float a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int lh = 1; lh < D / 8; lh <<= 1) {
+      const bool upper = (li & lh) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = wave_xor(x[e], lh);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+  }
+}
+
+constexpr int kPrepThreads = 256;
+constexpr int kRowsPerBlock = 256;
+
+// Per-head max |x| of the transformed rows.  grid = (ceil(N / 256), B*H).
+template <typename IT, int D, bool ROT, bool CENTER>
+__global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
+                                                       int32_t H, int32_t N, const float* __restrict__ mu_all,
+                                                       int32_t hq_per_mu, const int8_t* __restrict__ signs,
+                                                       uint32_t* __restrict__ amax, int32_t* __restrict__ status) {
+  constexpr int L = D / 8;                 // lanes per row
+  constexpr int RPI = kPrepThreads / L;    // rows per iteration
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int li = threadIdx.x % L, rl = threadIdx.x / L;
+  const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
+  const IT* base = x + b * sb + h * sh + 8 * li;
+  float m = 0.0f;
+  bool bad = false;
+  const int n_begin = blockIdx.x * kRowsPerBlock;
+  for (int r = rl; r < kRowsPerBlock; r += RPI) {
+    const int n = n_begin + r;
+    if (n >= N) break;
+    float v[8];
+    load8<IT>(base + static_cast<int64_t>(n) * sn, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(v[e]);
+    transform_row<D, ROT, CENTER>(v, li, mu, signs);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+  }
+  // Every lane of a row group takes part in the shuffles above, so rows past N
+  // must be skipped by the whole group together: the loop bound is uniform
+  // across the L lanes of a row (they share r).
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) m = __builtin_fmaxf(m, wave_xor(m, s));
+  __shared__ float red[kPrepThreads / kWave];
+  __shared__ int redbad;
+  if (threadIdx.x == 0) redbad = 0;
+  __syncthreads();
+  if (bad) atomicOr(&redbad, 1);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = red[0];
+    for (int w = 1; w < kPrepThreads / kWave; ++w) mm = __builtin_fmaxf(mm, red[w]);
+    atomicMax(amax + bh, __float_as_uint(mm));
+    if (redbad && status) atomicOr(status, 1);
+  }
+}
+
+__device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, float cd, float& inv, float& desc) {
+  const float A = __uint_as_float(abits);
+  if (A == 0.0f) { inv = 1.0f; desc = 1.0f; return; }
+  inv = 448.0f / A;
+  desc = A / 448.0f;
+  if (rotated) desc = desc * cd;
+}
+
+// Quantise Q or K rows into [B,H,Np,D] codes; rows in [N, Np) are written as 0.
+template <typename IT, int D, bool ROT, bool CENTER>
+__global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
+                                                             int32_t H, int32_t N, int32_t Np, const float* __restrict__ mu_all,
+                                                             int32_t hq_per_mu, const int8_t* __restrict__ signs,
+                                                             const uint32_t* __restrict__ amax, float cd,
+                                                             float* __restrict__ desc_out, uint8_t* __restrict__ codes) {
+  constexpr int L = D / 8;
+  constexpr int RPI = kPrepThreads / L;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int li = threadIdx.x % L, rl = threadIdx.x / L;
+  const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
+  float inv, desc;
+  scales_from_amax(amax[bh], ROT, cd, inv, desc);
+  if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+  const IT* base = x + b * sb + h * sh + 8 * li;
+  uint8_t* out = codes + static_cast<int64_t>(bh) * Np * D + 8 * li;
+  const int n_begin = blockIdx.x * kRowsPerBlock;
+  for (int r = rl; r < kRowsPerBlock; r += RPI) {
+    const int n = n_begin + r;
+    if (n >= Np) break;
+    uint2 w = make_uint2(0u, 0u);
+    if (n < N) {
+      float v[8];
+      load8<IT>(base + static_cast<int64_t>(n) * sn, v);
+      transform_row<D, ROT, CENTER>(v, li, mu, signs);
+      uint32_t lo = 0, hi = 0;
+      lo = e4m3_pack2<false>(v[0] * inv, v[1] * inv, lo);
+      lo = e4m3_pack2<true>(v[2] * inv, v[3] * inv, lo);
+      hi = e4m3_pack2<false>(v[4] * inv, v[5] * inv, hi);
+      hi = e4m3_pack2<true>(v[6] * inv, v[7] * inv, hi);
+      w = make_uint2(lo, hi);
+    }
+    *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
+  }
+}
+
+// Quantise V (never rotated) into the transposed layout [B,Hkv,D,Np]: one block
+// per 128 tokens of one head, staged through LDS so both the reads (rows) and
+// the writes (channel rows of 128 tokens) are contiguous.
+template <typename IT, int D>
+__global__ __launch_bounds__(kPrepThreads) void k_quant_vt(const IT* __restrict__ v, int64_t sb, int64_t sh, int64_t sn,
+                                                           int32_t H, int32_t N, int32_t Np,
+                                                           const uint32_t* __restrict__ amax,
+                                                           float* __restrict__ desc_out, uint8_t* __restrict__ v8t) {
+  constexpr int L = D / 8;
+  constexpr int RPI = kPrepThreads / L;
+  constexpr int TOK = 128;
+  constexpr int LDSW = TOK + 16;           // padded row of the channel-major tile
+  __shared__ __align__(16) uint8_t tile[D * LDSW];
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int li = threadIdx.x % L, rl = threadIdx.x / L;
+  float inv, desc;
+  scales_from_amax(amax[bh], false, 1.0f, inv, desc);
+  if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+  const IT* base = v + b * sb + h * sh + 8 * li;
+  const int n0 = blockIdx.x * TOK;
+  for (int r = rl; r < TOK; r += RPI) {
+    const int n = n0 + r;
+    uint32_t lo = 0, hi = 0;
+    if (n < N) {
+      float x[8];
+      load8<IT>(base + static_cast<int64_t>(n) * sn, x);
+      lo = e4m3_pack2<false>(x[0] * inv, x[1] * inv, lo);
+      lo = e4m3_pack2<true>(x[2] * inv, x[3] * inv, lo);
+      hi = e4m3_pack2<false>(x[4] * inv, x[5] * inv, hi);
+      hi = e4m3_pack2<true>(x[6] * inv, x[7] * inv, hi);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[(8 * li + e) * LDSW + r] = static_cast<uint8_t>(lo >> (8 * e));
+      tile[(8 * li + 4 + e) * LDSW + r] = static_cast<uint8_t>(hi >> (8 * e));
+    }
+  }
+  __syncthreads();
+  uint8_t* out = v8t + static_cast<int64_t>(bh) * D * Np + n0;
+  for (int e = threadIdx.x; e < D * (TOK / 16); e += kPrepThreads) {
+    const int c = e / (TOK / 16), j = e % (TOK / 16);
+    *reinterpret_cast<uint4*>(out + static_cast<int64_t>(c) * Np + 16 * j) =
+        *reinterpret_cast<const uint4*>(tile + c * LDSW + 16 * j);
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename IT, int D>
+static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
+  const dim3 blk(kPrepThreads);
+  const int32_t B = a.B, hq = a.hq, hkv = a.hkv, N = a.N, Np = a.Np;
+  const int32_t grp = hq / hkv;
+  const IT* q = static_cast<const IT*>(a.q);
+  const IT* k = static_cast<const IT*>(a.k);
+  const IT* v = static_cast<const IT*>(a.v);
+  const int64_t n_amax = static_cast<int64_t>(B) * (hq + 2 * hkv);
+  k_fill_u32<<<dim3(static_cast<unsigned>((n_amax + 255) / 256)), blk, 0, st>>>(a.amax, 0u, n_amax);
+  if (a.status) k_fill_u32<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<uint32_t*>(a.status), 0u, 1);
+  uint32_t* amax_q = a.amax;
+  uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq;
+  uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv;
+  if (a.center) {
+    k_kmean_partial<IT><<<dim3(a.np2, B * hkv), dim3(D), 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, D, a.np2, a.mean_part);
+    k_kmean_final<<<dim3(B * hkv), dim3(D), 0, st>>>(a.mean_part, a.np2, N, D, a.k_mean);
+  }
+  const dim3 gq((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
+  const dim3 gk((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
+  const dim3 gq_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
+  const dim3 gk_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
+  const float* mu = a.k_mean;
+  if (a.rotate) {
+    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, amax_q, a.status);
+    if (a.center)
+      k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, a.signs, amax_k, a.status);
+    else
+      k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, a.signs, amax_k, a.status);
+  } else {
+    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, amax_q, a.status);
+    if (a.center)
+      k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, amax_k, a.status);
+    else
+      k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, amax_k, a.status);
+  }
+  k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, amax_v, a.status);
+  if (a.rotate) {
+    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, amax_q, a.cd, a.q_desc, a.q8);
+    if (a.center)
+      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, amax_k, a.cd, a.k_desc, a.k8);
+    else
+      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, amax_k, a.cd, a.k_desc, a.k8);
+  } else {
+    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, amax_q, a.cd, a.q_desc, a.q8);
+    if (a.center)
+      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, amax_k, a.cd, a.k_desc, a.k8);
+    else
+      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, amax_k, a.cd, a.k_desc, a.k8);
+  }
+  k_quant_vt<IT, D><<<dim3(Np / 128, B * hkv), blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, Np, amax_v, a.v_desc, a.v8t);
+  (void)grp;
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st) {
+  if (a.bf16) {
+    if (a.D == 64) return launch_prepare_t<uint16_t, 64>(a, st);
+    return launch_prepare_t<uint16_t, 128>(a, st);
+  }
+  if (a.D == 64) return launch_prepare_t<float, 64>(a, st);
+  return launch_prepare_t<float, 128>(a, st);
+}
+
+}  // namespace fp8a

@@ -1,0 +1,89 @@
+"""Device-buffer plumbing around the C ABI: allocates with torch, then chains
+fp8_attn_prepare -> fp8_attn_fwd -> fp8_attn_head_error on one stream."""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+
+
+@dataclass
+class Prepared:
+    q8: torch.Tensor       # [B,hq,Np,d] uint8
+    k8: torch.Tensor       # [B,hkv,Np,d] uint8
+    v8t: torch.Tensor      # [B,hkv,d,Np] uint8
+    q_desc: torch.Tensor   # [B*hq] float32
+    k_desc: torch.Tensor   # [B*hkv]
+    v_desc: torch.Tensor   # [B*hkv]
+    k_mean: torch.Tensor   # [B*hkv*d] (valid after a centred prepare)
+    status: torch.Tensor   # [1] int32
+
+
+class AttnPipeline:
+    def __init__(self, batch: int, hq: int, hkv: int, seqlen: int, head_dim: int, device="cuda"):
+        self.B, self.hq, self.hkv, self.N, self.d = batch, hq, hkv, seqlen, head_dim
+        self.device = torch.device(device)
+        self.Np = _abi.padded_seqlen(seqlen)
+        self.shape = _abi.make_shape(batch, hq, hkv, seqlen, head_dim)
+        self._ws = {}
+
+    def _workspace(self, key, nbytes: int) -> torch.Tensor:
+        t = self._ws.get(key)
+        if t is None or t.numel() < nbytes:
+            t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = t
+        return t
+
+    def alloc_prepared(self) -> Prepared:
+        B, hq, hkv, Np, d, dev = self.B, self.hq, self.hkv, self.Np, self.d, self.device
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        return Prepared(torch.empty((B, hq, Np, d), **u8), torch.empty((B, hkv, Np, d), **u8),
+                        torch.empty((B, hkv, d, Np), **u8), torch.empty(B * hq, **f32),
+                        torch.empty(B * hkv, **f32), torch.empty(B * hkv, **f32),
+                        torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev))
+
+    def prepare(self, q, k, v, rotate: bool, center: bool, signs=None, prep: Prepared | None = None,
+                stream=None) -> Prepared:
+        prep = prep or self.alloc_prepared()
+        flags = (_abi.FP8A_ROTATE_QK if rotate else 0) | (_abi.FP8A_CENTER_K if center else 0)
+        shape = _abi.make_shape(self.B, self.hq, self.hkv, self.N, self.d, q, k, v)
+        ws = self._workspace("prep", _abi.prepare_workspace_bytes(shape, flags))
+        _abi.fp8_attn_prepare(shape, q, k, v, flags, signs if rotate else None, prep.q8, prep.k8, prep.v8t,
+                              prep.q_desc, prep.k_desc, prep.v_desc, prep.k_mean if center else None,
+                              prep.status, ws, stream)
+        return prep
+
+    def fwd(self, prep: Prepared, p_scale: float = 256.0, kv_order: int = 1, block_n: int = 128,
+            causal: bool = True, softmax_scale: float | None = None, out=None, lse=None, p_dump=None,
+            row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.d)
+        if out is None:
+            out = torch.empty((self.B, self.hq, self.N, self.d), dtype=torch.float32, device=self.device)
+        _abi.fp8_attn_fwd(self.shape, _abi.FP8A_E4M3, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
+                          prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse, p_dump,
+                          row_zeros, k_sink, stream)
+        return out
+
+    def fwd_f32(self, q, k, v, p_scale: float = 256.0, kv_order: int = 0, block_n: int = 128,
+                causal: bool = False, softmax_scale: float | None = None, out=None, lse=None, p_dump=None,
+                row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(self.d)
+        if out is None:
+            out = torch.empty((self.B, self.hq, self.N, self.d), dtype=torch.float32, device=self.device)
+        _abi.fp8_attn_fwd(self.shape, _abi.FP8A_F32, q, k, v, None, None, None, softmax_scale, p_scale, kv_order,
+                          block_n, int(causal), out, lse, p_dump, row_zeros, k_sink, stream)
+        return out
+
+    def head_error(self, out, ref, rows=None, rel_err=None, stream=None) -> torch.Tensor:
+        nrows = self.N if rows is None else int(rows.numel())
+        ws = self._workspace("err", _abi.head_error_workspace_bytes(self.shape, nrows))
+        if rel_err is None:
+            rel_err = torch.empty(self.B * self.hq, dtype=torch.float64, device=self.device)
+        _abi.fp8_attn_head_error(self.shape, out, ref, rows, nrows, rel_err, ws, stream)
+        return rel_err

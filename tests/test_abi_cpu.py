@@ -1,0 +1,139 @@
+"""The C-ABI library on the host: it loads, exports every function
+include/fp8_attn.h declares, and its host-side validation rejects bad
+arguments before any launch (no GPU is touched: every call below fails a check
+that precedes the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "precision_attention_numerics_amd", "libfp8attn.so")
+HEADER = os.path.join(ROOT, "include", "fp8_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfp8attn.so is not built: run __graft_entry__.build()")
+    return ctypes.CDLL(LIB)
+
+
+@pytest.fixture(scope="module")
+def abi():
+    import precision_attention_numerics_amd._abi as abi
+    return abi
+
+
+def declared():
+    return sorted(set(re.findall(r"\b(fp8_attn_\w+)\s*\(", open(HEADER).read())))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for must in ("fp8_attn_prepare", "fp8_attn_fwd", "fp8_attn_head_error", "fp8_attn_strerror"):
+        assert must in names
+
+
+def test_every_declared_symbol_exported(lib):
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("torch types", "") and "at::" not in text
+
+
+def test_pure_host_helpers(abi):
+    assert abi.padded_seqlen(1) == 128 and abi.padded_seqlen(128) == 128 and abi.padded_seqlen(129) == 256
+    assert abi.padded_seqlen(0) == 0
+    for st in range(-6, 1):
+        assert abi.strerror(st) != "unknown status"
+    assert abi.strerror(-99) == "unknown status"
+
+
+def test_workspace_sizes(abi):
+    s = abi.make_shape(1, 32, 8, 32768, 128)
+    base = abi.prepare_workspace_bytes(s, 0)
+    cen = abi.prepare_workspace_bytes(s, abi.FP8A_CENTER_K)
+    assert base >= (32 + 16) * 4 and cen > base
+    assert cen - base >= 8 * 512 * 128 * 8          # 512 chunk partials per KV head and channel
+    assert abi.head_error_workspace_bytes(s, 32768) >= 32 * 2 * 8
+    bad = abi.make_shape(1, 3, 2, 16, 128)           # hq % hkv != 0
+    assert abi.prepare_workspace_bytes(bad, 0) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: every call fails validation first
+
+
+def _no_gpu():
+    """The fake-pointer calls are only made where no GPU is visible, so that a
+    validation bug could never turn into a launch on real hardware."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run on hosts without a GPU")
+
+
+def _prep(abi, shape, dtype=1, flags=0, signs=FAKE, ws=FAKE, ws_bytes=1 << 30, q=FAKE):
+    return abi._lib.fp8_attn_prepare(ctypes.byref(shape), dtype, q, FAKE, FAKE, flags, signs, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, None, None, ws, ws_bytes, None)
+
+
+def _fwd(abi, shape, **kw):
+    a = dict(dtype=3, scale=0.088, S=256.0, order=1, bn=128, causal=1, out=FAKE, k_sink=0, desc=FAKE)
+    a.update(kw)
+    return abi._lib.fp8_attn_fwd(ctypes.byref(shape), a["dtype"], FAKE, FAKE, FAKE, a["desc"], a["desc"], a["desc"],
+                                 a["scale"], a["S"], a["order"], a["bn"], a["causal"], a["out"], None, None, None,
+                                 a["k_sink"], None)
+
+
+def test_prepare_rejects(abi):
+    _no_gpu()
+    ok = abi.make_shape(1, 2, 1, 64, 64)
+    assert _prep(abi, abi.make_shape(1, 2, 1, 64, 96)) == -2          # head_dim
+    assert _prep(abi, abi.make_shape(1, 3, 2, 64, 64)) == -2          # GQA ratio
+    assert _prep(abi, abi.make_shape(0, 2, 1, 64, 64)) == -2          # batch
+    assert _prep(abi, abi.make_shape(1, 2, 1, 0, 64)) == -2           # seqlen
+    assert _prep(abi, ok, dtype=2) == -3                               # f64 input
+    assert _prep(abi, ok, flags=8) == -4                               # unknown flag
+    assert _prep(abi, ok, q=None) == -1
+    assert _prep(abi, ok, flags=abi.FP8A_ROTATE_QK, signs=None) == -1
+    assert _prep(abi, ok, ws=None) == -5
+    assert _prep(abi, ok, ws_bytes=1) == -5
+    assert _prep(abi, ok, q=ctypes.c_void_p((1 << 20) + 8)) == -2     # misaligned
+    st = abi.make_shape(1, 2, 1, 64, 64)
+    st.q_stride[:] = [8192, 4096, 63]                                  # row stride not a multiple of 8
+    assert _prep(abi, st) == -2
+    assert abi._lib.fp8_attn_prepare(None, 1, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     None, None, FAKE, 1 << 30, None) == -1
+
+
+def test_fwd_rejects(abi):
+    _no_gpu()
+    ok = abi.make_shape(1, 2, 1, 64, 64)
+    assert _fwd(abi, ok, bn=96) == -4
+    assert _fwd(abi, ok, order=2) == -4
+    assert _fwd(abi, ok, causal=3) == -4
+    assert _fwd(abi, ok, scale=0.0) == -4
+    assert _fwd(abi, ok, scale=float("nan")) == -4
+    assert _fwd(abi, ok, S=0.0) == -4
+    assert _fwd(abi, ok, S=500.0) == -4
+    assert _fwd(abi, ok, S=100.0) == -3                                 # not a power of two nor 448
+    assert _fwd(abi, ok, S=0.5) == -3
+    assert _fwd(abi, ok, k_sink=-1) == -4
+    assert _fwd(abi, ok, dtype=1) == -3                                 # bf16 operands go through prepare
+    assert _fwd(abi, ok, desc=None) == -1
+    assert _fwd(abi, ok, out=None) == -1
+    assert _fwd(abi, abi.make_shape(1, 2, 1, 64, 32)) == -2
+
+
+def test_head_error_rejects(abi):
+    _no_gpu()
+    ok = abi.make_shape(1, 2, 1, 64, 64)
+    f = abi._lib.fp8_attn_head_error
+    assert f(ctypes.byref(ok), FAKE, FAKE, 0, None, 63, FAKE, FAKE, 1 << 20, None) == -2   # nrows != N without rows
+    assert f(ctypes.byref(ok), FAKE, FAKE, 1, None, 64, FAKE, FAKE, 1 << 20, None) == -3   # bf16 reference
+    assert f(ctypes.byref(ok), None, FAKE, 0, None, 64, FAKE, FAKE, 1 << 20, None) == -1
+    assert f(ctypes.byref(ok), FAKE, FAKE, 0, None, 64, FAKE, None, 0, None) == -5
