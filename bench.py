@@ -42,7 +42,21 @@ def parse():
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sample-tiles", type=int, default=3, help="query tiles per head in the CPU sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy (read + write of this many MiB), for scaling HBM counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int, steps: int):
+    """A plain elementwise copy kernel of known size: reads and writes mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4, "launches": steps}))
 
 
 def sample_rows(N: int, tiles: int) -> np.ndarray:
@@ -61,6 +75,10 @@ def main():
               "Per-head sharding would need no communication; see the design notes.", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, args.steps)
+        return
 
     import precision_attention_numerics_amd as pan
     import synth

@@ -176,6 +176,12 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
   p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.Np = fp8_attn_padded_seqlen(s->seqlen);
   p.n_qtiles = p.Np / 128; p.kv_order = kv_order; p.k_sink = k_sink;
   p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
+  {
+    float x0, x1;
+    memcpy(&x0, &bad0, 4);
+    memcpy(&x1, &bad1, 4);
+    p.xcheck = x0 < x1 ? x0 : x1;
+  }
   const bool dump = p_dump != nullptr || row_zeros != nullptr;
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));
 }

@@ -27,19 +27,23 @@ namespace fp8a {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 
+// 16-byte register type (a clang vector, so private arrays of it stay in
+// registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ v8i lds_read32(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
   v8i r;
-  r[0] = static_cast<int>(a.x); r[1] = static_cast<int>(a.y); r[2] = static_cast<int>(a.z); r[3] = static_cast<int>(a.w);
-  r[4] = static_cast<int>(b.x); r[5] = static_cast<int>(b.y); r[6] = static_cast<int>(b.z); r[7] = static_cast<int>(b.w);
+  r[0] = static_cast<int>(a[0]); r[1] = static_cast<int>(a[1]); r[2] = static_cast<int>(a[2]); r[3] = static_cast<int>(a[3]);
+  r[4] = static_cast<int>(b[0]); r[5] = static_cast<int>(b[1]); r[6] = static_cast<int>(b[2]); r[7] = static_cast<int>(b[3]);
   return r;
 }
 
 __device__ __forceinline__ v8i lds_read16_pad(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
   v8i r;
-  r[0] = static_cast<int>(a.x); r[1] = static_cast<int>(a.y); r[2] = static_cast<int>(a.z); r[3] = static_cast<int>(a.w);
+  r[0] = static_cast<int>(a[0]); r[1] = static_cast<int>(a[1]); r[2] = static_cast<int>(a[2]); r[3] = static_cast<int>(a[3]);
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
 }
@@ -60,19 +64,167 @@ __device__ __forceinline__ float exp2_code_exact(float x, uint32_t bad0, uint32_
   return p;
 }
 
+// LDS tiles are stored in 16-byte units with an XOR swizzle of the unit
+// index inside each row, so that the 16 rows one MFMA operand read touches
+// fall into different banks.  Tiles are filled by direct global->LDS DMA:
+// one wave instruction writes 64 consecutive units, each lane fetching the
+// global chunk that belongs in its unit.
+template <int UNITS>
+__device__ __forceinline__ int swz(int row) {
+  return (row ^ (row >> 3)) & (UNITS - 1);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// K tile [BC rows][D bytes] of block blk and V^T tile [D rows][BC bytes].
+// The per-lane part of each address is a 32-bit offset (the same for every
+// block); the block's base is wave-uniform.
+template <int D, int BC>
+__device__ __attribute__((always_inline)) inline void dma_kv_tile(const uint8_t* __restrict__ kbase,
+                                                                 const uint8_t* __restrict__ vbase, int Np, int blk,
+                                                                 int wv, int lane, uint8_t* kbuf, uint8_t* vbuf) {
+  constexpr int UK = D / 16, UV = BC / 16;
+  constexpr int KI = BC * UK / 64 / kWaves;   // wave instructions per tile
+  constexpr int VI = D * UV / 64 / kWaves;
+  const uint8_t* kblk = kbase + static_cast<int64_t>(blk) * BC * D;
+  const uint8_t* vblk = vbase + static_cast<int64_t>(blk) * BC;
+#pragma unroll
+  for (int e = 0; e < KI; ++e) {
+    const int u0 = (wv * KI + e) * 64;
+    const int u = u0 + lane;
+    const int row = u / UK, col = (u % UK) ^ swz<UK>(row);
+    const uint32_t off = static_cast<uint32_t>(row * D + 16 * col);
+    __builtin_amdgcn_global_load_lds(kblk + off, (lds_ptr_t)(kbuf + 16 * u0), 16, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < VI; ++e) {
+    const int u0 = (wv * VI + e) * 64;
+    const int u = u0 + lane;
+    const int row = u / UV, col = (u % UV) ^ swz<UV>(row);
+    const uint32_t off = static_cast<uint32_t>(row * Np + 16 * col);
+    __builtin_amdgcn_global_load_lds(vblk + off, (lds_ptr_t)(vbuf + 16 * u0), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ v8i lds_read_units(const uint8_t* base, int u_a, int u_b) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(base + 16 * u_a);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(base + 16 * u_b);
+  v8i r;
+  r[0] = static_cast<int>(a[0]); r[1] = static_cast<int>(a[1]); r[2] = static_cast<int>(a[2]); r[3] = static_cast<int>(a[3]);
+  r[4] = static_cast<int>(b[0]); r[5] = static_cast<int>(b[1]); r[6] = static_cast<int>(b[2]); r[7] = static_cast<int>(b[3]);
+  return r;
+}
+
+// Online-softmax update and P cast for one 16-row query tile and one block:
+// the lane holds query i and keys jb + 4t + r (t < T, r < 4).  MASK selects
+// the per-key visibility test (diagonal and ragged blocks only); CHECK the
+// exp fix-up test (only blocks whose largest x can reach the listed x
+// values).  Returns the packed E4M3 codes in the operand order of the P.V
+// instruction.
+template <int T, bool MASK, bool CHECK, bool CAUSAL, bool POW2, bool DUMP>
+__device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T], const float c, const float nmc,
+                                                               float& lsum, const int i, const int jb, const int N,
+                                                               const FwdParams& p, uint32_t& zeros,
+                                                               uint8_t* __restrict__ dump_row) {
+  v8i out;
+  float part[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = __builtin_fmaf(s[t][r], c, nmc);
+      float pv = __builtin_amdgcn_exp2f(x);
+      if constexpr (CHECK) {
+        const uint32_t xb = __float_as_uint(x);
+        if ((xb == p.bad0) | (xb == p.bad1)) pv = static_cast<float>(exp2(static_cast<double>(x)));
+      }
+      if constexpr (MASK) {
+        const int j = jb + 4 * t + r;
+        pv = ((j < N) && (!CAUSAL || j <= i)) ? pv : 0.0f;
+      }
+      pr[r] = pv;
+    }
+    part[t] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    uint32_t w = 0;
+    if constexpr (POW2) {
+      w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
+      w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
+    } else {
+      w = e4m3_pack2<false>(pr[0] * p.S, pr[1] * p.S, w);
+      w = e4m3_pack2<true>(pr[2] * p.S, pr[3] * p.S, w);
+    }
+    out[t] = static_cast<int>(w);
+    if constexpr (DUMP) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + 4 * t + r;
+        const bool vis = (j < N) && (!CAUSAL || j <= i);
+        const uint32_t code = (w >> (8 * r)) & 0xFFu;
+        if (vis && j >= p.k_sink && code == 0u) ++zeros;
+        if (dump_row && i < N && j < N) dump_row[j] = static_cast<uint8_t>(code);
+      }
+    }
+  }
+  // row sum of this lane's keys, pairwise (the order only affects l's rounding)
+#pragma unroll
+  for (int w = T / 2; w > 0; w >>= 1)
+#pragma unroll
+    for (int t = 0; t < w; ++t) part[t] = part[t] + part[t + w];
+  lsum = lsum + part[0];
+#pragma unroll
+  for (int t = T; t < 8; ++t) out[t] = 0;
+  return out;
+}
+
+template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
+__device__ __attribute__((always_inline)) inline v8i softmax_tile(const v4f (&s)[T], const float c, float& ms, float& mcp,
+                                                                  float& lsum, v4f (&oacc)[D / 16], const int i,
+                                                                  const int jb, const int N, const FwdParams& p,
+                                                                  uint32_t& zeros, uint8_t* __restrict__ dump_row) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float sv = s[t][r];
+      if constexpr (MASK) {
+        const int j = jb + 4 * t + r;
+        sv = ((j < N) && (!CAUSAL || j <= i)) ? sv : -INFINITY;
+      }
+      bm = __builtin_fmaxf(bm, sv);
+    }
+  bm = __builtin_fmaxf(bm, wave_xor(bm, 16));
+  bm = __builtin_fmaxf(bm, wave_xor(bm, 32));
+  const float mnew = __builtin_fmaxf(ms, bm);
+  const float mc = (mnew == -INFINITY) ? 0.0f : mnew * c;
+  const float alpha = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mcp - mc);
+  lsum = lsum * alpha;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) oacc[ct] *= alpha;
+  }
+  ms = mnew;
+  mcp = mc;
+  const float nmc = -mc;
+  // Every x of this row is at most fma(bm, c, -mc) (the max commutes with the
+  // monotone fma).  The fix-up is needed only where that bound reaches the
+  // listed x, which happens in few blocks (those holding keys near the max).
+  const bool check = __any((bm != -INFINITY) && (__builtin_fmaf(bm, c, nmc) >= p.xcheck));
+  if (check) return cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, c, nmc, lsum, i, jb, N, p, zeros, dump_row);
+  return cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, c, nmc, lsum, i, jb, N, p, zeros, dump_row);
+}
+
 template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   constexpr int QROWS = kWaves * QT * 16;
   static_assert(QROWS == 128, "query tile must match the 128-token padding");
   constexpr int T = BC / 16;          // 16-key MFMA tiles per block
   constexpr int KPL = BC / 4;         // keys per accumulator lane group
-  constexpr int KST = D + 16;         // padded LDS row of the K tile
-  constexpr int VST = BC + 16;        // padded LDS row of the V^T tile
-  constexpr int KLD = BC * D / 16 / kThreads;  // 16-byte loads per thread
-  constexpr int VLD = D * BC / 16 / kThreads;
-  static_assert(KLD >= 1 && VLD >= 1, "tile too small for the workgroup");
-  __shared__ __align__(16) uint8_t klds[BC * KST];
-  __shared__ __align__(16) uint8_t vlds[D * VST];
+  constexpr int UK = D / 16, UV = BC / 16;   // 16-byte units per LDS row of the K and V^T tiles
+  static_assert(BC * UK % (64 * kWaves) == 0 && D * UV % (64 * kWaves) == 0, "tile must split into wave DMAs");
+  __shared__ __align__(16) uint8_t klds[2][BC * D];
+  __shared__ __align__(16) uint8_t vlds[2][D * BC];
 
   // ---- workgroup -> (batch*head, query tile)
   const int BH = p.B * p.hq;
@@ -133,128 +285,65 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   const uint8_t* kbase = p.k8 + static_cast<int64_t>(bg) * Np * D;
   const uint8_t* vbase = p.v8t + static_cast<int64_t>(bg) * D * Np;
 
-  uint4 kreg[KLD], vreg[VLD];
-  auto gload = [&](int blk) {
-    const int j0 = blk * BC;
-#pragma unroll
-    for (int e = 0; e < KLD; ++e) {
-      const int idx = tid + e * kThreads;
-      const int row = idx / (D / 16), col = idx % (D / 16);
-      kreg[e] = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(j0 + row) * D + 16 * col);
-    }
-#pragma unroll
-    for (int e = 0; e < VLD; ++e) {
-      const int idx = tid + e * kThreads;
-      const int row = idx / (BC / 16), col = idx % (BC / 16);
-      vreg[e] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(row) * Np + j0 + 16 * col);
-    }
-  };
-  gload(p.kv_order ? jmax : 0);
+  dma_kv_tile<D, BC>(kbase, vbase, Np, p.kv_order ? jmax : 0, wv, lane, klds[0], vlds[0]);
 
   for (int it = 0; it <= jmax; ++it) {
     const int blk = p.kv_order ? jmax - it : it;
     const int j0 = blk * BC;
-    __syncthreads();  // the previous tile has been consumed by every wave
-#pragma unroll
-    for (int e = 0; e < KLD; ++e) {
-      const int idx = tid + e * kThreads;
-      const int row = idx / (D / 16), col = idx % (D / 16);
-      *reinterpret_cast<uint4*>(klds + row * KST + 16 * col) = kreg[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VLD; ++e) {
-      const int idx = tid + e * kThreads;
-      const int row = idx / (BC / 16), col = idx % (BC / 16);
-      *reinterpret_cast<uint4*>(vlds + row * VST + 16 * col) = vreg[e];
-    }
+    const int cur = it & 1;
+    // This wave's DMA into the current buffers has landed; the barrier makes
+    // every wave's share visible and ends all reads of the other buffers.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (it < jmax) gload(p.kv_order ? jmax - it - 1 : it + 1);
+    if (it < jmax) dma_kv_tile<D, BC>(kbase, vbase, Np, p.kv_order ? jmax - it - 1 : it + 1, wv, lane,
+                                      klds[cur ^ 1], vlds[cur ^ 1]);
+    const uint8_t* kt = klds[cur];
+    const uint8_t* vt = vlds[cur];
 
-    // ---- S^T tiles: key tile t, A row m = n16 -> key KPL*(m/4) + 4t + m%4
-    v4f sacc[QT][T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int jj = KPL * (n16 >> 2) + 4 * t + (n16 & 3);
-      v8i a;
-      if (32 * lg < D) {
-        a = lds_read32(klds + jj * KST + 32 * lg);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = 0;
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sacc[qt][t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-    }
-
-    // ---- online softmax and the P cast; lane holds query n16, keys j0 + KPL*lg + 4t + r
+    // ---- per 16-row query tile: S^T = K Q^T (A row m = n16 -> key KPL*(m/4) + 4t + m%4),
+    // then the online softmax and the P cast; the lane ends up holding query
+    // n16 and keys j0 + KPL*lg + 4t + r.
+    const int wrow0 = q0 + wv * QT * 16;
+    const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wrow0);
     v8i pop[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const int i = q0 + wv * QT * 16 + qt * 16 + n16;
-      float bm = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + KPL * lg + 4 * t + r;
-          const bool vis = (j < N) && (!CAUSAL || j <= i);
-          bm = __builtin_fmaxf(bm, vis ? sacc[qt][t][r] : -INFINITY);
-        }
-      bm = __builtin_fmaxf(bm, wave_xor(bm, 16));
-      bm = __builtin_fmaxf(bm, wave_xor(bm, 32));
-      const float mnew = __builtin_fmaxf(ms[qt], bm);
-      const float mc = (mnew == -INFINITY) ? 0.0f : mnew * c;
-      const float alpha = (ms[qt] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mcp[qt] - mc);
-      lsum[qt] = lsum[qt] * alpha;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int ct = 0; ct < D / 16; ++ct) oacc[qt][ct] *= alpha;
-      }
-      ms[qt] = mnew;
-      mcp[qt] = mc;
-      const float nmc = -mc;
+      v4f sacc[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + KPL * lg + 4 * t + r;
-          const bool vis = (j < N) && (!CAUSAL || j <= i);
-          const float x = __builtin_fmaf(sacc[qt][t][r], c, nmc);
-          const float pv = exp2_code_exact(x, p.bad0, p.bad1);
-          pr[r] = vis ? pv : 0.0f;
-          lsum[qt] += pr[r];
-        }
-        uint32_t w = 0;
-        if constexpr (POW2) {
-          w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
-          w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
+        const int jj = KPL * (n16 >> 2) + 4 * t + (n16 & 3);
+        v8i a;
+        if (32 * lg < D) {
+          const int sw = swz<UK>(jj);
+          a = lds_read_units(kt, jj * UK + ((2 * lg) ^ sw), jj * UK + ((2 * lg + 1) ^ sw));
         } else {
-          w = e4m3_pack2<false>(pr[0] * p.S, pr[1] * p.S, w);
-          w = e4m3_pack2<true>(pr[2] * p.S, pr[3] * p.S, w);
-        }
-        pop[qt][t] = static_cast<int>(w);
-        if constexpr (DUMP) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + KPL * lg + 4 * t + r;
-            const bool vis = (j < N) && (!CAUSAL || j <= i);
-            const uint32_t code = (w >> (8 * r)) & 0xFFu;
-            if (vis && j >= p.k_sink && code == 0u) ++zeros[qt];
-            if (p.p_dump && i < N && j < N)
-              p.p_dump[(static_cast<int64_t>(bh) * N + i) * N + j] = static_cast<uint8_t>(code);
-          }
+          for (int e = 0; e < 8; ++e) a[e] = 0;
         }
+        sacc[t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
       }
-#pragma unroll
-      for (int t = T; t < 8; ++t) pop[qt][t] = 0;
+      const int i = wrow0 + qt * 16 + n16;
+      uint8_t* drow = nullptr;
+      if constexpr (DUMP) drow = p.p_dump ? p.p_dump + (static_cast<int64_t>(bh) * N + i) * N : nullptr;
+      if (DUMP || need_mask)
+        pop[qt] = softmax_tile<D, T, true, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
+                                                              j0 + KPL * lg, N, p, zeros[qt], drow);
+      else
+        pop[qt] = softmax_tile<D, T, false, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
+                                                               j0 + KPL * lg, N, p, zeros[qt], drow);
     }
 
     // ---- O^T += V^T P^T: A row = channel 16 ct + n16, keys [KPL lg, KPL lg + KPL)
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) {
-      const uint8_t* src = vlds + (16 * ct + n16) * VST + KPL * lg;
-      const v8i a = (KPL == 32) ? lds_read32(src) : lds_read16_pad(src);
+      const int cr = 16 * ct + n16;
+      const int sw = swz<UV>(cr);
+      v8i a;
+      if constexpr (KPL == 32) {
+        a = lds_read_units(vt, cr * UV + ((2 * lg) ^ sw), cr * UV + ((2 * lg + 1) ^ sw));
+      } else {
+        a = lds_read16_pad(vt + 16 * (cr * UV + (lg ^ sw)));
+      }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) oacc[qt][ct] = mfma_f8(a, pop[qt], oacc[qt][ct]);
     }
