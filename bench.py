@@ -59,6 +59,24 @@ def copy_calibration(mib: int, steps: int):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4, "launches": steps}))
 
 
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of the forward kernel from the committed rocprofv3
+    counters (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the kernel
+    source has changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_long_context_32k.json")
+    src = os.path.join(ROOT, "precision_attention_numerics_amd", "csrc", "attn_fwd.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    for name, v in rec["kernels"].items():
+        if name.startswith(kernel):
+            return v.get("read_bytes", 0.0) + v.get("write_bytes", 0.0)
+    return None
+
+
 def sample_rows(N: int, tiles: int) -> np.ndarray:
     """First, middle and last 128-row query tiles (evenly spaced tiles when
     more are asked for)."""
@@ -194,7 +212,8 @@ def main():
                                "BF16 sink-generator operands (Delta=8, 4 sinks), S=256, reverse KV order, block 128" % N,
                    "condition": "centered_rotated", "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
+                     "traffic": profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false>"),
                      "kernel": "k_attn_fwd<128,128,2,causal,pow2>", "flop_per_launch": flop},
         "cpu_baseline": cpu,
         "detail": results,

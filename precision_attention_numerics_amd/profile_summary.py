@@ -1,6 +1,9 @@
 """Summarise rocprofv3 CSV output of bench.py runs into a short text table.
 
 usage: python -m precision_attention_numerics_amd.profile_summary PROFDIR > summary.md
+       python -m precision_attention_numerics_amd.profile_summary PROFDIR --json OUT.json
+(the JSON records the forward kernel's scaled HBM bytes per launch and the
+sha256 of the kernel source they were measured on)
 
 PROFDIR holds the sub-directories written by these commands (run from /tmp,
 TMPDIR=/tmp, R = repository root):
@@ -75,5 +78,29 @@ def main(d: str):
             print(f"  VALU instructions per MFMA: {g.get('SQ_INSTS_VALU', 0) / max(g.get('SQ_INSTS_MFMA', 1), 1):.2f}")
 
 
+def write_json(d: str, out: str):
+    import hashlib
+    import json
+    fetch = counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
+    write = counters(os.path.join(d, "write", "write_counter_collection.csv"))
+    copyf = counters(os.path.join(d, "copyf", "copyf_counter_collection.csv"))
+    copyw = counters(os.path.join(d, "copyw", "copyw_counter_collection.csv"))
+    f_scale = COPY_BYTES / (max(v for (k, c), v in copyf.items() if "elementwise" in k) * 1024)
+    w_scale = COPY_BYTES / (max(v for (k, c), v in copyw.items() if "elementwise" in k) * 1024)
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "attn_fwd.hip")
+    res = {"kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(), "kernels": {}}
+    for (k, c), v in fetch.items():
+        if "k_attn_fwd" in k:
+            res["kernels"].setdefault(k, {})["read_bytes"] = v * 1024 * f_scale
+    for (k, c), v in write.items():
+        if "k_attn_fwd" in k:
+            res["kernels"].setdefault(k, {})["write_bytes"] = v * 1024 * w_scale
+    res["fetch_scale"], res["write_scale"] = f_scale, w_scale
+    json.dump(res, open(out, "w"), indent=1)
+
+
 if __name__ == "__main__":
-    main(sys.argv[1])
+    if "--json" in sys.argv:
+        write_json(sys.argv[1], sys.argv[sys.argv.index("--json") + 1])
+    else:
+        main(sys.argv[1])
