@@ -72,6 +72,10 @@ bool p_scale_setup(float S, bool* pow2, float* inv_S, uint32_t* bad0, uint32_t* 
   return false;
 }
 
+// 2^x rounded once to binary32 (the binary64 exp2 is accurate to well under
+// the distance of these 2^x from a binary32 rounding boundary).
+float rn32_exp2(float x) { return static_cast<float>(exp2(static_cast<double>(x))); }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8A_OK : FP8A_ERR_HIP; }
 
 }  // namespace
@@ -181,6 +185,8 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
     memcpy(&x0, &bad0, 4);
     memcpy(&x1, &bad1, 4);
     p.xcheck = x0 < x1 ? x0 : x1;
+    p.fix0 = rn32_exp2(x0);
+    p.fix1 = rn32_exp2(x1);
   }
   const bool dump = p_dump != nullptr || row_zeros != nullptr;
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));

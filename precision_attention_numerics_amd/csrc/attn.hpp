@@ -22,6 +22,7 @@ struct FwdParams {
   float inv_S;            // 1/S when S is a power of two
   uint32_t bad0, bad1;    // binary32 patterns of x whose v_exp_f32 result would flip a code
   float xcheck;           // smaller of the two listed x: blocks whose largest x is below it need no fix-up
+  float fix0, fix1;       // RN32(2^x) for the two listed x
 };
 
 struct PcastParams {

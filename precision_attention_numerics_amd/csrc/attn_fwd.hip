@@ -117,17 +117,19 @@ __device__ __forceinline__ v8i lds_read_units(const uint8_t* base, int u_a, int 
 
 // Online-softmax update and P cast for one 16-row query tile and one block:
 // the lane holds query i and keys jb + 4t + r (t < T, r < 4).  MASK selects
-// the per-key visibility test (diagonal and ragged blocks only); CHECK the
-// exp fix-up test (only blocks whose largest x can reach the listed x
-// values).  Returns the packed E4M3 codes in the operand order of the P.V
-// instruction.
-template <int T, bool MASK, bool CHECK, bool CAUSAL, bool POW2, bool DUMP>
+// the per-key visibility test (diagonal and ragged blocks only).  MODE 0
+// casts with v_exp_f32; MODE 2 replaces the result for the two listed x by
+// their correctly rounded 2^x (only run when a wave has such an x).
+// Returns the packed E4M3 codes in the operand order of the P.V instruction;
+// lpart is this lane's sum of p and zpart its count of zero codes.
+template <int T, bool MASK, int MODE, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T], const float c, const float nmc,
-                                                               float& lsum, const int i, const int jb, const int N,
-                                                               const FwdParams& p, uint32_t& zeros,
+                                                               float& lpart, uint32_t& zpart, bool& bad, const int i,
+                                                               const int jb, const int N, const FwdParams& p,
                                                                uint8_t* __restrict__ dump_row) {
   v8i out;
   float part[T];
+  uint32_t zeros = 0;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     float pr[4];
@@ -135,9 +137,10 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T]
     for (int r = 0; r < 4; ++r) {
       const float x = __builtin_fmaf(s[t][r], c, nmc);
       float pv = __builtin_amdgcn_exp2f(x);
-      if constexpr (CHECK) {
+      if constexpr (MODE == 2) {
         const uint32_t xb = __float_as_uint(x);
-        if ((xb == p.bad0) | (xb == p.bad1)) pv = static_cast<float>(exp2(static_cast<double>(x)));
+        pv = (xb == p.bad0) ? p.fix0 : pv;
+        pv = (xb == p.bad1) ? p.fix1 : pv;
       }
       if constexpr (MASK) {
         const int j = jb + 4 * t + r;
@@ -171,7 +174,8 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T]
   for (int w = T / 2; w > 0; w >>= 1)
 #pragma unroll
     for (int t = 0; t < w; ++t) part[t] = part[t] + part[t + w];
-  lsum = lsum + part[0];
+  lpart = part[0];
+  zpart = zeros;
 #pragma unroll
   for (int t = T; t < 8; ++t) out[t] = 0;
   return out;
@@ -208,11 +212,29 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(const v4f (&s)
   mcp = mc;
   const float nmc = -mc;
   // Every x of this row is at most fma(bm, c, -mc) (the max commutes with the
-  // monotone fma).  The fix-up is needed only where that bound reaches the
-  // listed x, which happens in few blocks (those holding keys near the max).
+  // monotone fma).  The listed x can only occur where that bound reaches them,
+  // i.e. in blocks holding keys near the running max.
   const bool check = __any((bm != -INFINITY) && (__builtin_fmaf(bm, c, nmc) >= p.xcheck));
-  if (check) return cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, c, nmc, lsum, i, jb, N, p, zeros, dump_row);
-  return cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, c, nmc, lsum, i, jb, N, p, zeros, dump_row);
+  float lpart;
+  uint32_t zpart;
+  bool bad = false;
+  if (check) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t xb = __float_as_uint(__builtin_fmaf(s[t][r], c, nmc));
+        bad |= (xb == p.bad0) | (xb == p.bad1);
+      }
+  }
+  v8i out;
+  if (__builtin_expect(__any(bad), 0))
+    out = cast_tile<T, MASK, 2, CAUSAL, POW2, DUMP>(s, c, nmc, lpart, zpart, bad, i, jb, N, p, dump_row);
+  else
+    out = cast_tile<T, MASK, 0, CAUSAL, POW2, DUMP>(s, c, nmc, lpart, zpart, bad, i, jb, N, p, dump_row);
+  lsum = lsum + lpart;
+  zeros += zpart;
+  return out;
 }
 
 template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP>
