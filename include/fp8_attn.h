@@ -134,6 +134,8 @@ int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
  *              unvisited blocks are left untouched, so zero it first.
  *   row_zeros  device out, uint32 [B,hq,N] (may be NULL): number of visible
  *              keys j >= k_sink whose P~ code is 0.
+ * Errors: FP8A_ERR_SHAPE also when, with E4M3 operands, one head's codes
+ * (Np*d bytes) exceed 2^31 - 1.
  */
 int fp8_attn_fwd(const fp8a_shape* shape, fp8a_dtype qkv_dtype,
                  const void* q, const void* k, const void* v,

@@ -148,6 +148,11 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
   if (rc) return rc;
   if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32) return FP8A_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out) return FP8A_ERR_NULL;
+  // the E4M3 kernel addresses one head's K8 / V8t through a buffer resource
+  // with a 31-bit byte range
+  if (qkv_dtype == FP8A_E4M3 &&
+      static_cast<int64_t>(fp8_attn_padded_seqlen(s->seqlen)) * s->head_dim > INT32_MAX)
+    return FP8A_ERR_SHAPE;
   if (qkv_dtype == FP8A_E4M3 && (!q_desc || !k_desc || !v_desc)) return FP8A_ERR_NULL;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FP8A_ERR_PARAM;
   if (!(p_scale > 0.0f) || !(p_scale <= 448.0f)) return FP8A_ERR_PARAM;

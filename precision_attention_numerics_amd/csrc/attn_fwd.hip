@@ -31,15 +31,6 @@ constexpr int kThreads = kWaves * kWave;
 // registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v8i lds_read32(const uint8_t* p) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
-  v8i r;
-  r[0] = static_cast<int>(a[0]); r[1] = static_cast<int>(a[1]); r[2] = static_cast<int>(a[2]); r[3] = static_cast<int>(a[3]);
-  r[4] = static_cast<int>(b[0]); r[5] = static_cast<int>(b[1]); r[6] = static_cast<int>(b[2]); r[7] = static_cast<int>(b[3]);
-  return r;
-}
-
 __device__ __forceinline__ v8i lds_read16_pad(const uint8_t* p) {
   const u32x4 a = *reinterpret_cast<const u32x4*>(p);
   v8i r;
@@ -64,69 +55,122 @@ __device__ __forceinline__ float exp2_code_exact(float x, uint32_t bad0, uint32_
   return p;
 }
 
-// LDS tiles are stored in 16-byte units with an XOR swizzle of the unit
-// index inside each row, so that the 16 rows one MFMA operand read touches
-// fall into different banks.  Tiles are filled by direct global->LDS DMA:
-// one wave instruction writes 64 consecutive units, each lane fetching the
-// global chunk that belongs in its unit.
-template <int UNITS>
-__device__ __forceinline__ int swz(int row) {
-  return (row ^ (row >> 3)) & (UNITS - 1);
+// LDS tiles are stored in 16-byte units; unit u of row r sits at position
+// u ^ swz(r) of its row.  The swizzles use only the row-index bits that differ
+// between the 16 lanes of one ds_read_b128 phase (never the key or channel
+// tile index), so that (a) each phase touches 16 distinct 4-bank groups of the
+// 64 banks and (b) every tile is read at a constant offset from one per-lane
+// base address.  Tiles are filled by direct global->LDS DMA: one wave
+// instruction writes 64 consecutive units, each lane fetching the global chunk
+// that belongs in its unit.
+//
+// K tile: row r = key within the block; the 16 lanes of a phase read rows
+// KPL*q + 4t + b (q = n16 >> 2, b = n16 & 3).
+template <int D, int BC>
+__device__ __forceinline__ int swz_k(int r) {
+  constexpr int KPL = BC / 4;
+  const int q = (r / KPL) & 3;
+  if constexpr (D == 128) return ((r >> 1) & 1) | ((q & 1) << 1) | ((((r & 1) ^ (q >> 1)) & 1) << 2);
+  else return q;
+}
+// V^T tile: row r = channel; a phase reads rows 16 ct + n16.
+template <int BC>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (BC == 128) return ((r >> 1) & 3) | ((((r >> 3) ^ r) & 1) << 2);
+  else return (r >> 2) & 3;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// K tile [BC rows][D bytes] of block blk and V^T tile [D rows][BC bytes].
-// The per-lane part of each address is a 32-bit offset (the same for every
-// block); the block's base is wave-uniform.
-template <int D, int BC>
-__device__ __attribute__((always_inline)) inline void dma_kv_tile(const uint8_t* __restrict__ kbase,
-                                                                 const uint8_t* __restrict__ vbase, int Np, int blk,
-                                                                 int wv, int lane, uint8_t* kbuf, uint8_t* vbuf) {
-  constexpr int UK = D / 16, UV = BC / 16;
-  constexpr int KI = BC * UK / 64 / kWaves;   // wave instructions per tile
-  constexpr int VI = D * UV / 64 / kWaves;
-  const uint8_t* kblk = kbase + static_cast<int64_t>(blk) * BC * D;
-  const uint8_t* vblk = vbase + static_cast<int64_t>(blk) * BC;
-#pragma unroll
-  for (int e = 0; e < KI; ++e) {
-    const int u0 = (wv * KI + e) * 64;
-    const int u = u0 + lane;
-    const int row = u / UK, col = (u % UK) ^ swz<UK>(row);
-    const uint32_t off = static_cast<uint32_t>(row * D + 16 * col);
-    __builtin_amdgcn_global_load_lds(kblk + off, (lds_ptr_t)(kbuf + 16 * u0), 16, 0, 0);
-  }
-#pragma unroll
-  for (int e = 0; e < VI; ++e) {
-    const int u0 = (wv * VI + e) * 64;
-    const int u = u0 + lane;
-    const int row = u / UV, col = (u % UV) ^ swz<UV>(row);
-    const uint32_t off = static_cast<uint32_t>(row * Np + 16 * col);
-    __builtin_amdgcn_global_load_lds(vblk + off, (lds_ptr_t)(vbuf + 16 * u0), 16, 0, 0);
-  }
+// Buffer resource over one head's bytes (raw buffer: stride 0, byte offsets;
+// loads past num_records return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
 }
 
-__device__ __forceinline__ v8i lds_read_units(const uint8_t* base, int u_a, int u_b) {
-  const u32x4 a = *reinterpret_cast<const u32x4*>(base + 16 * u_a);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(base + 16 * u_b);
+// Tile fills by buffer_load ... lds: wave wv issues instructions w = wv*KI + e
+// (K) and w = wv*VI + e (V^T); instruction w writes units [64w, 64w + 64) of
+// the tile, lane l the unit 64w + l.  For K, the rows of one wave all have
+// r / KPL == wv and the swizzle bits come from the lane alone, so one lane
+// offset serves every instruction (+1 KB each); for V^T the swizzle depends
+// on the parity of w at BC = 128, hence two lane offsets.
+template <int D, int BC>
+struct KvFill {
+  static constexpr int UK = D / 16, UV = BC / 16;
+  static constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
+  static constexpr int KPL = BC / 4;
+  uint32_t koff, voff0, voff1;
+
+  __device__ __forceinline__ void init(int wv, int lane, int Np) {
+    {
+      // row wv*KPL + lane/UK of the block: the wave's part (wv*KPL rows) is
+      // added as a scalar offset in issue(); the swizzle needs the full row
+      const int row = lane / UK;
+      koff = static_cast<uint32_t>(row * D + 16 * ((lane % UK) ^ swz_k<D, BC>(wv * KPL + row)));
+    }
+    const int r0 = lane / UV;                 // row within the instruction
+    const int r1 = r0 + 64 / UV;              // the same lane in an odd instruction
+    voff0 = static_cast<uint32_t>(r0 * Np + 16 * ((lane % UV) ^ swz_v<BC>(r0)));
+    voff1 = static_cast<uint32_t>(r0 * Np + 16 * ((lane % UV) ^ swz_v<BC>(r1)));
+  }
+
+  // K tile [BC rows][D bytes] and V^T tile [D rows][BC bytes] of block blk.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int Np, int blk,
+                                        int wv, uint8_t* kbuf, uint8_t* vbuf) const {
+    const uint32_t kblk = static_cast<uint32_t>(blk) * (BC * D) + static_cast<uint32_t>(wv * KPL * D);
+#pragma unroll
+    for (int e = 0; e < KI; ++e)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI + e)), 16, koff,
+                                               kblk + static_cast<uint32_t>(e * 1024), 0, 0);
+#pragma unroll
+    for (int e = 0; e < VI; ++e) {
+      const int w = wv * VI + e;
+      const uint32_t vblk = static_cast<uint32_t>(blk) * BC + static_cast<uint32_t>(w * (64 / UV)) * Np;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * w), 16, (e & 1) ? voff1 : voff0, vblk,
+                                               0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ v8i lds_read_pair(const uint8_t* p0, const uint8_t* p1) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p1);
   v8i r;
   r[0] = static_cast<int>(a[0]); r[1] = static_cast<int>(a[1]); r[2] = static_cast<int>(a[2]); r[3] = static_cast<int>(a[3]);
   r[4] = static_cast<int>(b[0]); r[5] = static_cast<int>(b[1]); r[6] = static_cast<int>(b[2]); r[7] = static_cast<int>(b[3]);
   return r;
 }
 
-// Online-softmax update and P cast for one 16-row query tile and one block:
-// the lane holds query i and keys jb + 4t + r (t < T, r < 4).  MASK selects
-// the per-key visibility test (diagonal and ragged blocks only).  MODE 0
-// casts with v_exp_f32; MODE 2 replaces the result for the two listed x by
-// their correctly rounded 2^x (only run when a wave has such an x).
-// Returns the packed E4M3 codes in the operand order of the P.V instruction;
-// lpart is this lane's sum of p and zpart its count of zero codes.
-template <int T, bool MASK, int MODE, bool CAUSAL, bool POW2, bool DUMP>
-__device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T], const float c, const float nmc,
-                                                               float& lpart, uint32_t& zpart, bool& bad, const int i,
-                                                               const int jb, const int N, const FwdParams& p,
-                                                               uint8_t* __restrict__ dump_row) {
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950; unlike fmaxf it
+// needs no quieting of its inputs).  Scores are finite or -inf here.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum over the four lane groups that hold one query column (lanes l,
+// l^16, l^32, l^48): each swap step exchanges halves of a register pair, and
+// the max of the pair is the xor-partner combination.
+__device__ __forceinline__ float column_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float column_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// P = 2^x for the tile's x (in place in s), sum of this lane's P into lpart,
+// E4M3 codes of S*P packed in the operand order of the P.V instruction.
+// FIX replaces the exp result for the two listed x by their correctly rounded
+// values (only run when a wave holds such an x).  MASK zeroes invisible keys.
+template <int T, bool MASK, bool FIX, bool CAUSAL, bool POW2, bool DUMP>
+__device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T], float& lpart, uint32_t& zpart,
+                                                               const int lim, const int i, const int jb, const int N,
+                                                               const FwdParams& p, uint8_t* __restrict__ dump_row) {
   v8i out;
   float part[T];
   uint32_t zeros = 0;
@@ -135,21 +179,18 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T]
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x = __builtin_fmaf(s[t][r], c, nmc);
-      float pv = __builtin_amdgcn_exp2f(x);
-      if constexpr (MODE == 2) {
-        const uint32_t xb = __float_as_uint(x);
+      float pv = __builtin_amdgcn_exp2f(x[t][r]);
+      if constexpr (FIX) {
+        const uint32_t xb = __float_as_uint(x[t][r]);
         pv = (xb == p.bad0) ? p.fix0 : pv;
         pv = (xb == p.bad1) ? p.fix1 : pv;
       }
-      if constexpr (MASK) {
-        const int j = jb + 4 * t + r;
-        pv = ((j < N) && (!CAUSAL || j <= i)) ? pv : 0.0f;
-      }
+      if constexpr (MASK) pv = (4 * t + r < lim) ? pv : 0.0f;
       pr[r] = pv;
     }
     part[t] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    uint32_t w = 0;
+    // both halves of w are written below; its initial bits are never used
+    uint32_t w = __builtin_nondeterministic_value(w);
     if constexpr (POW2) {
       w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
       w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
@@ -181,57 +222,65 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&s)[T]
   return out;
 }
 
+// Online-softmax update of one 16-row query tile for one block and the P
+// cast.  The lane holds query i and keys jb + 4t + r (t < T, r < 4); s holds
+// the scores on entry and x = s*c - RN32(m*c) on exit.
 template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
-__device__ __attribute__((always_inline)) inline v8i softmax_tile(const v4f (&s)[T], const float c, float& ms, float& mcp,
+__device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], const float c, float& ms, float& mcp,
                                                                   float& lsum, v4f (&oacc)[D / 16], const int i,
                                                                   const int jb, const int N, const FwdParams& p,
                                                                   uint32_t& zeros, uint8_t* __restrict__ dump_row) {
-  float bm = -INFINITY;
+  // key jb + k is visible iff k < lim (k = 4t + r): one compare per key
+  const int lim = min(N, CAUSAL ? i + 1 : N) - jb;
+  if constexpr (MASK) {
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float sv = s[t][r];
-      if constexpr (MASK) {
-        const int j = jb + 4 * t + r;
-        sv = ((j < N) && (!CAUSAL || j <= i)) ? sv : -INFINITY;
-      }
-      bm = __builtin_fmaxf(bm, sv);
-    }
-  bm = __builtin_fmaxf(bm, wave_xor(bm, 16));
-  bm = __builtin_fmaxf(bm, wave_xor(bm, 32));
-  const float mnew = __builtin_fmaxf(ms, bm);
+      for (int r = 0; r < 4; ++r) s[t][r] = (4 * t + r < lim) ? s[t][r] : -INFINITY;
+  }
+  float m4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m4[r] = s[0][r];
+#pragma unroll
+    for (int t = 1; t < T; ++t) m4[r] = fmax_nan(m4[r], s[t][r]);
+  }
+  const float bm = column_max(fmax_nan(fmax_nan(m4[0], m4[1]), fmax_nan(m4[2], m4[3])));
+  const float mnew = fmax_nan(ms, bm);
   const float mc = (mnew == -INFINITY) ? 0.0f : mnew * c;
   const float alpha = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mcp - mc);
   lsum = lsum * alpha;
-  if (__any(alpha != 1.0f)) {
+  // Unconditional: alpha is exactly 1 when the max did not move, and a
+  // branch here makes the compiler keep two copies of O.
 #pragma unroll
-    for (int ct = 0; ct < D / 16; ++ct) oacc[ct] *= alpha;
-  }
+  for (int ct = 0; ct < D / 16; ++ct) oacc[ct] *= alpha;
   ms = mnew;
   mcp = mc;
   const float nmc = -mc;
-  // Every x of this row is at most fma(bm, c, -mc) (the max commutes with the
-  // monotone fma).  The listed x can only occur where that bound reaches them,
-  // i.e. in blocks holding keys near the running max.
-  const bool check = __any((bm != -INFINITY) && (__builtin_fmaf(bm, c, nmc) >= p.xcheck));
-  float lpart;
-  uint32_t zpart;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[t][r] = __builtin_fmaf(s[t][r], c, nmc);
+  // Every x of this row is at most fma(bm, c, -mc) (the fma is monotone in s
+  // for c > 0): the listed x can only occur in blocks holding keys near the
+  // running max, and only there is each x compared with them.
   bool bad = false;
-  if (check) {
+  if (__any(__builtin_fmaf(bm, c, nmc) >= p.xcheck)) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t xb = __float_as_uint(__builtin_fmaf(s[t][r], c, nmc));
+        const uint32_t xb = __float_as_uint(s[t][r]);
         bad |= (xb == p.bad0) | (xb == p.bad1);
       }
   }
+  float lpart;
+  uint32_t zpart;
   v8i out;
   if (__builtin_expect(__any(bad), 0))
-    out = cast_tile<T, MASK, 2, CAUSAL, POW2, DUMP>(s, c, nmc, lpart, zpart, bad, i, jb, N, p, dump_row);
+    out = cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
   else
-    out = cast_tile<T, MASK, 0, CAUSAL, POW2, DUMP>(s, c, nmc, lpart, zpart, bad, i, jb, N, p, dump_row);
+    out = cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
   return out;
@@ -244,9 +293,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   constexpr int T = BC / 16;          // 16-key MFMA tiles per block
   constexpr int KPL = BC / 4;         // keys per accumulator lane group
   constexpr int UK = D / 16, UV = BC / 16;   // 16-byte units per LDS row of the K and V^T tiles
+  constexpr int KBYTES = BC * D;
   static_assert(BC * UK % (64 * kWaves) == 0 && D * UV % (64 * kWaves) == 0, "tile must split into wave DMAs");
-  __shared__ __align__(16) uint8_t klds[2][BC * D];
-  __shared__ __align__(16) uint8_t vlds[2][D * BC];
+  __shared__ __align__(16) uint8_t klds[2 * KBYTES];
+  __shared__ __align__(16) uint8_t vlds[2 * KBYTES];
 
   // ---- workgroup -> (batch*head, query tile)
   const int BH = p.B * p.hq;
@@ -271,15 +321,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   const float c = (p.q_desc[bh] * p.k_desc[bg]) * p.ls2;
   const float vdesc = p.v_desc[bg];
 
-  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  // wv is wave-uniform; readfirstlane lets the compiler keep it (and every
+  // per-block decision made from it) in scalar registers.
+  const int tid = threadIdx.x, lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n16 = lane & 15, lg = lane >> 4;
+  const bool has_k = 32 * lg < D;     // lane groups past head_dim feed zeros (head_dim 64)
 
   // ---- Q operand (B of S^T = K Q^T): query row n16, channels [32 lg, 32 lg + 32)
   v8i qop[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int i = q0 + wv * QT * 16 + qt * 16 + n16;
-    if (32 * lg < D) {
+    if (has_k) {
       const uint8_t* src = p.q8 + (static_cast<int64_t>(bh) * Np + i) * D + 32 * lg;
       const uint4 a = *reinterpret_cast<const uint4*>(src);
       const uint4 bb = *reinterpret_cast<const uint4*>(src + 16);
@@ -290,6 +343,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       for (int e = 0; e < 8; ++e) qop[qt][e] = 0;
     }
   }
+
+  // ---- per-lane LDS read offsets (tile t / channel tile ct add constants)
+  // K: A row m = n16 of tile t -> key KPL*(m/4) + 4t + m%4, channels [32 lg, 32 lg + 32)
+  const int jj0 = KPL * (n16 >> 2) + (n16 & 3);
+  const int kofs0 = 16 * (jj0 * UK + ((2 * lg) ^ swz_k<D, BC>(jj0)));
+  const int kofs1 = 16 * (jj0 * UK + ((2 * lg + 1) ^ swz_k<D, BC>(jj0)));
+  // V^T: A row = channel 16 ct + n16, keys [KPL lg, KPL lg + KPL)
+  const int vofs0 = 16 * (n16 * UV + ((KPL == 32 ? 2 * lg : lg) ^ swz_v<BC>(n16)));
+  const int vofs1 = 16 * (n16 * UV + ((2 * lg + 1) ^ swz_v<BC>(n16)));
 
   // ---- running state per query tile (replicated over the 4 lane groups)
   float ms[QT], mcp[QT], lsum[QT];
@@ -304,28 +366,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 
   const int q_last = min(q0 + QROWS - 1, N - 1);
   const int jmax = CAUSAL ? q_last / BC : (N - 1) / BC;
-  const uint8_t* kbase = p.k8 + static_cast<int64_t>(bg) * Np * D;
-  const uint8_t* vbase = p.v8t + static_cast<int64_t>(bg) * D * Np;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k8 + static_cast<int64_t>(bg) * Np * D, static_cast<uint32_t>(Np) * D);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v8t + static_cast<int64_t>(bg) * D * Np, static_cast<uint32_t>(Np) * D);
+  const int wrow0 = q0 + wv * QT * 16;
+  KvFill<D, BC> fill;
+  fill.init(wv, lane, Np);
 
-  dma_kv_tile<D, BC>(kbase, vbase, Np, p.kv_order ? jmax : 0, wv, lane, klds[0], vlds[0]);
+  fill.issue(krs, vrs, Np, p.kv_order ? jmax : 0, wv, klds, vlds);
 
   for (int it = 0; it <= jmax; ++it) {
     const int blk = p.kv_order ? jmax - it : it;
     const int j0 = blk * BC;
-    const int cur = it & 1;
+    const int cur = (it & 1) * KBYTES;
     // This wave's DMA into the current buffers has landed; the barrier makes
     // every wave's share visible and ends all reads of the other buffers.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (it < jmax) dma_kv_tile<D, BC>(kbase, vbase, Np, p.kv_order ? jmax - it - 1 : it + 1, wv, lane,
-                                      klds[cur ^ 1], vlds[cur ^ 1]);
-    const uint8_t* kt = klds[cur];
-    const uint8_t* vt = vlds[cur];
+    if (it < jmax) fill.issue(krs, vrs, Np, p.kv_order ? jmax - it - 1 : it + 1, wv, klds + (KBYTES - cur),
+                              vlds + (KBYTES - cur));
+    const uint8_t* kt = klds + cur;
+    const uint8_t* vt = vlds + cur;
 
-    // ---- per 16-row query tile: S^T = K Q^T (A row m = n16 -> key KPL*(m/4) + 4t + m%4),
-    // then the online softmax and the P cast; the lane ends up holding query
-    // n16 and keys j0 + KPL*lg + 4t + r.
-    const int wrow0 = q0 + wv * QT * 16;
+    // ---- per 16-row query tile: S^T = K Q^T, then the online softmax and the
+    // P cast; the lane ends up holding query n16 and keys j0 + KPL*lg + 4t + r.
     const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wrow0);
     v8i pop[QT];
 #pragma unroll
@@ -333,11 +396,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       v4f sacc[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const int jj = KPL * (n16 >> 2) + 4 * t + (n16 & 3);
         v8i a;
-        if (32 * lg < D) {
-          const int sw = swz<UK>(jj);
-          a = lds_read_units(kt, jj * UK + ((2 * lg) ^ sw), jj * UK + ((2 * lg + 1) ^ sw));
+        if (has_k) {
+          a = lds_read_pair(kt + kofs0 + t * 64 * UK, kt + kofs1 + t * 64 * UK);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) a[e] = 0;
@@ -355,16 +416,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
                                                                j0 + KPL * lg, N, p, zeros[qt], drow);
     }
 
-    // ---- O^T += V^T P^T: A row = channel 16 ct + n16, keys [KPL lg, KPL lg + KPL)
+    // ---- O^T += V^T P^T
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) {
-      const int cr = 16 * ct + n16;
-      const int sw = swz<UV>(cr);
       v8i a;
       if constexpr (KPL == 32) {
-        a = lds_read_units(vt, cr * UV + ((2 * lg) ^ sw), cr * UV + ((2 * lg + 1) ^ sw));
+        a = lds_read_pair(vt + vofs0 + ct * 256 * UV, vt + vofs1 + ct * 256 * UV);
       } else {
-        a = lds_read16_pad(vt + 16 * (cr * UV + (lg ^ sw)));
+        a = lds_read16_pad(vt + vofs0 + ct * 256 * UV);
       }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) oacc[qt][ct] = mfma_f8(a, pop[qt], oacc[qt][ct]);
@@ -375,9 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int i = q0 + wv * QT * 16 + qt * 16 + n16;
-    float l = lsum[qt];
-    l += wave_xor(l, 16);
-    l += wave_xor(l, 32);
+    const float l = column_sum(lsum[qt]);
     const float f = vdesc / (p.S * l);
     if (i < N) {
       float* orow = p.out + (static_cast<int64_t>(bh) * N + i) * D;
