@@ -189,8 +189,9 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
       pr[r] = pv;
     }
     part[t] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    // both halves of w are written below; its initial bits are never used
-    uint32_t w = __builtin_nondeterministic_value(w);
+    // both halves of w are written below, so its initial bits are never
+    // used; seeding it from a value that is dead by then avoids a move
+    uint32_t w = __float_as_uint(pr[0]);
     if constexpr (POW2) {
       w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
       w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
@@ -263,21 +264,27 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
     for (int r = 0; r < 4; ++r) s[t][r] = __builtin_fmaf(s[t][r], c, nmc);
   // Every x of this row is at most fma(bm, c, -mc) (the fma is monotone in s
   // for c > 0): the listed x can only occur in blocks holding keys near the
-  // running max, and only there is each x compared with them.
-  bool bad = false;
+  // running max, and only there is each x screened.  (xb ^ B0) & (xb ^ B1) is
+  // zero whenever xb is B0 or B1 (and for the few patterns that agree with B0
+  // or B1 bit by bit, which only cost a slower but still exact cast): one
+  // bit-op per x and a min over pairs, all in vector registers.  A wave
+  // holding a zero takes the cast that compares each x with the two patterns.
+  bool fix = false;
   if (__any(__builtin_fmaf(bm, c, nmc) >= p.xcheck)) {
+    uint32_t acc = 0xFFFFFFFFu;
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t xb = __float_as_uint(s[t][r]);
-        bad |= (xb == p.bad0) | (xb == p.bad1);
+        acc = min(acc, (xb ^ p.bad0) & (xb ^ p.bad1));
       }
+    fix = __any(acc == 0u);
   }
   float lpart;
   uint32_t zpart;
   v8i out;
-  if (__builtin_expect(__any(bad), 0))
+  if (__builtin_expect(fix, 0))
     out = cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
   else
     out = cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
