@@ -17,6 +17,9 @@ FLAGS = [
     # no packed FP32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
+    # a symbol left undefined (e.g. a kernel launch stub the host pass did not
+    # emit) fails the build instead of the first load
+    "-Wl,--no-undefined",
 ]
 
 

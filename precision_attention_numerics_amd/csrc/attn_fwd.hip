@@ -55,29 +55,30 @@ __device__ __forceinline__ float exp2_code_exact(float x, uint32_t bad0, uint32_
   return p;
 }
 
-// LDS tiles are stored in 16-byte units; unit u of row r sits at position
-// u ^ swz(r) of its row.  The swizzles use only the row-index bits that differ
-// between the 16 lanes of one ds_read_b128 phase (never the key or channel
-// tile index), so that (a) each phase touches 16 distinct 4-bank groups of the
-// 64 banks and (b) every tile is read at a constant offset from one per-lane
-// base address.  Tiles are filled by direct global->LDS DMA: one wave
-// instruction writes 64 consecutive units, each lane fetching the global chunk
-// that belongs in its unit.
+// LDS tiles are stored in 16-byte units; unit u of LDS row r sits at
+// position u ^ swz(r mod 16) of its row.  Every operand read has the same
+// shape: the 16 lanes of a lane group read LDS rows 16*tile + n16, so the
+// swizzle depends on n16 alone and each tile is read at a constant offset from
+// one per-lane base.  For 128-byte rows the swizzle (n0^n3, n1, n2) was chosen
+// by measuring ds_read_b128 throughput on gfx950 (full rate, like a linear
+// read); for 64-byte rows no 2-bit XOR swizzle reaches full rate and
+// (n0^n3, n1^n2) is among the best measured.
 //
-// K tile: row r = key within the block; the 16 lanes of a phase read rows
-// KPL*q + 4t + b (q = n16 >> 2, b = n16 & 3).
-template <int D, int BC>
-__device__ __forceinline__ int swz_k(int r) {
-  constexpr int KPL = BC / 4;
-  const int q = (r / KPL) & 3;
-  if constexpr (D == 128) return ((r >> 1) & 1) | ((q & 1) << 1) | ((((r & 1) ^ (q >> 1)) & 1) << 2);
-  else return q;
+// K rows are permuted in LDS: key jj of the block (jj = KPL*q + 4t + b, the
+// row of MFMA tile t that lane n16 = 4q + b holds) sits at LDS row
+// 16t + n16.  V^T rows (channels) are stored in order.  Tiles are filled by
+// direct buffer->LDS DMA: one wave instruction writes 64 consecutive units,
+// each lane fetching the global chunk that belongs in its unit.
+template <int U>
+__device__ __forceinline__ int swz(int n) {
+  if constexpr (U == 8) return ((n ^ (n >> 3)) & 1) | (n & 6);
+  else return ((n ^ (n >> 3)) & 1) | ((((n >> 1) ^ (n >> 2)) & 1) << 1);
 }
-// V^T tile: row r = channel; a phase reads rows 16 ct + n16.
+
+// key (within the block) stored at LDS row r of the K tile
 template <int BC>
-__device__ __forceinline__ int swz_v(int r) {
-  if constexpr (BC == 128) return ((r >> 1) & 3) | ((((r >> 3) ^ r) & 1) << 2);
-  else return (r >> 2) & 3;
+__device__ __forceinline__ int key_of_row(int r) {
+  return (BC / 4) * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -91,47 +92,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* base,
 
 // Tile fills by buffer_load ... lds: wave wv issues instructions w = wv*KI + e
 // (K) and w = wv*VI + e (V^T); instruction w writes units [64w, 64w + 64) of
-// the tile, lane l the unit 64w + l.  For K, the rows of one wave all have
-// r / KPL == wv and the swizzle bits come from the lane alone, so one lane
-// offset serves every instruction (+1 KB each); for V^T the swizzle depends
-// on the parity of w at BC = 128, hence two lane offsets.
+// the tile, lane l the unit 64w + l.  The lane's global offsets within a block
+// are fixed per (wave, e) and computed once (fill_offsets); each block adds a
+// uniform base (fill_issue).  The offset arrays are the kernel's locals
+// (KI and VI entries); after inlining they stay in registers.
 template <int D, int BC>
-struct KvFill {
-  static constexpr int UK = D / 16, UV = BC / 16;
-  static constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
-  static constexpr int KPL = BC / 4;
-  uint32_t koff, voff0, voff1;
-
-  __device__ __forceinline__ void init(int wv, int lane, int Np) {
-    {
-      // row wv*KPL + lane/UK of the block: the wave's part (wv*KPL rows) is
-      // added as a scalar offset in issue(); the swizzle needs the full row
-      const int row = lane / UK;
-      koff = static_cast<uint32_t>(row * D + 16 * ((lane % UK) ^ swz_k<D, BC>(wv * KPL + row)));
-    }
-    const int r0 = lane / UV;                 // row within the instruction
-    const int r1 = r0 + 64 / UV;              // the same lane in an odd instruction
-    voff0 = static_cast<uint32_t>(r0 * Np + 16 * ((lane % UV) ^ swz_v<BC>(r0)));
-    voff1 = static_cast<uint32_t>(r0 * Np + 16 * ((lane % UV) ^ swz_v<BC>(r1)));
-  }
-
-  // K tile [BC rows][D bytes] and V^T tile [D rows][BC bytes] of block blk.
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int Np, int blk,
-                                        int wv, uint8_t* kbuf, uint8_t* vbuf) const {
-    const uint32_t kblk = static_cast<uint32_t>(blk) * (BC * D) + static_cast<uint32_t>(wv * KPL * D);
+__device__ __forceinline__ void fill_offsets(int wv, int lane, int Np, uint32_t* koff, uint32_t* voff) {
+  constexpr int UK = D / 16, UV = BC / 16;
+  constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
 #pragma unroll
-    for (int e = 0; e < KI; ++e)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI + e)), 16, koff,
-                                               kblk + static_cast<uint32_t>(e * 1024), 0, 0);
-#pragma unroll
-    for (int e = 0; e < VI; ++e) {
-      const int w = wv * VI + e;
-      const uint32_t vblk = static_cast<uint32_t>(blk) * BC + static_cast<uint32_t>(w * (64 / UV)) * Np;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * w), 16, (e & 1) ? voff1 : voff0, vblk,
-                                               0, 0);
-    }
+  for (int e = 0; e < KI; ++e) {
+    const int u = 64 * (wv * KI + e) + lane;
+    const int r = u / UK;
+    koff[e] = static_cast<uint32_t>(key_of_row<BC>(r) * D + 16 * ((u % UK) ^ swz<UK>(r & 15)));
   }
-};
+#pragma unroll
+  for (int e = 0; e < VI; ++e) {
+    const int u = 64 * (wv * VI + e) + lane;
+    const int r = u / UV;
+    voff[e] = static_cast<uint32_t>(r * Np + 16 * ((u % UV) ^ swz<UV>(r & 15)));
+  }
+}
+
+// K tile [BC rows][D bytes] and V^T tile [D rows][BC bytes] of block blk;
+// kbase / vbase are the head's K8 and V8t (head_bytes each).  (The buffer
+// resources are built here, from the uniform base pointers.)
+template <int D, int BC>
+__device__ __forceinline__ void fill_issue(const uint8_t* kbase, const uint8_t* vbase, uint32_t head_bytes, int blk,
+                                           int wv, const uint32_t* koff, const uint32_t* voff, uint8_t* kbuf,
+                                           uint8_t* vbuf) {
+  constexpr int UK = D / 16, UV = BC / 16;
+  constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kbase, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vbase, head_bytes);
+  const uint32_t kblk = static_cast<uint32_t>(blk) * (BC * D);
+  const uint32_t vblk = static_cast<uint32_t>(blk) * BC;
+#pragma unroll
+  for (int e = 0; e < KI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI + e)), 16, koff[e], kblk, 0, 0);
+#pragma unroll
+  for (int e = 0; e < VI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * (wv * VI + e)), 16, voff[e], vblk, 0, 0);
+}
 
 __device__ __forceinline__ v8i lds_read_pair(const uint8_t* p0, const uint8_t* p1) {
   const u32x4 a = *reinterpret_cast<const u32x4*>(p0);
@@ -352,13 +354,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   }
 
   // ---- per-lane LDS read offsets (tile t / channel tile ct add constants)
-  // K: A row m = n16 of tile t -> key KPL*(m/4) + 4t + m%4, channels [32 lg, 32 lg + 32)
-  const int jj0 = KPL * (n16 >> 2) + (n16 & 3);
-  const int kofs0 = 16 * (jj0 * UK + ((2 * lg) ^ swz_k<D, BC>(jj0)));
-  const int kofs1 = 16 * (jj0 * UK + ((2 * lg + 1) ^ swz_k<D, BC>(jj0)));
+  // K: A row m = n16 of tile t -> key KPL*(m/4) + 4t + m%4 = LDS row 16t + n16,
+  // channels [32 lg, 32 lg + 32)
+  const int kofs0 = 16 * (n16 * UK + ((2 * lg) ^ swz<UK>(n16)));
+  const int kofs1 = 16 * (n16 * UK + ((2 * lg + 1) ^ swz<UK>(n16)));
   // V^T: A row = channel 16 ct + n16, keys [KPL lg, KPL lg + KPL)
-  const int vofs0 = 16 * (n16 * UV + ((KPL == 32 ? 2 * lg : lg) ^ swz_v<BC>(n16)));
-  const int vofs1 = 16 * (n16 * UV + ((2 * lg + 1) ^ swz_v<BC>(n16)));
+  const int vofs0 = 16 * (n16 * UV + ((KPL == 32 ? 2 * lg : lg) ^ swz<UV>(n16)));
+  const int vofs1 = 16 * (n16 * UV + ((2 * lg + 1) ^ swz<UV>(n16)));
 
   // ---- running state per query tile (replicated over the 4 lane groups)
   float ms[QT], mcp[QT], lsum[QT];
@@ -373,13 +375,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 
   const int q_last = min(q0 + QROWS - 1, N - 1);
   const int jmax = CAUSAL ? q_last / BC : (N - 1) / BC;
-  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k8 + static_cast<int64_t>(bg) * Np * D, static_cast<uint32_t>(Np) * D);
-  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v8t + static_cast<int64_t>(bg) * D * Np, static_cast<uint32_t>(Np) * D);
+  const uint8_t* kbase = p.k8 + static_cast<int64_t>(bg) * Np * D;
+  const uint8_t* vbase = p.v8t + static_cast<int64_t>(bg) * D * Np;
+  const uint32_t head_bytes = static_cast<uint32_t>(Np) * D;
   const int wrow0 = q0 + wv * QT * 16;
-  KvFill<D, BC> fill;
-  fill.init(wv, lane, Np);
+  uint32_t koff[BC * D / 16 / 64 / kWaves], voff[D * BC / 16 / 64 / kWaves];
+  fill_offsets<D, BC>(wv, lane, Np, koff, voff);
 
-  fill.issue(krs, vrs, Np, p.kv_order ? jmax : 0, wv, klds, vlds);
+  fill_issue<D, BC>(kbase, vbase, head_bytes, p.kv_order ? jmax : 0, wv, koff, voff, klds, vlds);
 
   for (int it = 0; it <= jmax; ++it) {
     const int blk = p.kv_order ? jmax - it : it;
@@ -389,8 +392,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
     // every wave's share visible and ends all reads of the other buffers.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (it < jmax) fill.issue(krs, vrs, Np, p.kv_order ? jmax - it - 1 : it + 1, wv, klds + (KBYTES - cur),
-                              vlds + (KBYTES - cur));
+    if (it < jmax)
+      fill_issue<D, BC>(kbase, vbase, head_bytes, p.kv_order ? jmax - it - 1 : it + 1, wv, koff, voff,
+                        klds + (KBYTES - cur),
+                        vlds + (KBYTES - cur));
     const uint8_t* kt = klds + cur;
     const uint8_t* vt = vlds + cur;
 
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       for (int t = 0; t < T; ++t) {
         v8i a;
         if (has_k) {
-          a = lds_read_pair(kt + kofs0 + t * 64 * UK, kt + kofs1 + t * 64 * UK);
+          a = lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) a[e] = 0;
