@@ -46,37 +46,99 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t value, int64_t n) 
   if (i < n) p[i] = value;
 }
 
-// Partial sums of the mean key: one block per (chunk of 64 tokens, KV head),
-// one thread per channel; tokens are added in increasing order in binary64
-// starting from +0.0.  Chunks in [nchunk, np2) are the tree's zero padding.
-template <typename IT>
-__global__ void k_kmean_partial(const IT* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
-                                int32_t hkv, int32_t N, int32_t D, int32_t np2, double* __restrict__ part) {
-  const int32_t t = blockIdx.x, bg = blockIdx.y, c = threadIdx.x;
-  if (c >= D) return;
+// Partial sums of the mean key: each group of D/8 lanes owns one chunk of 64
+// tokens of one KV head, 8 channels per lane; tokens are added in increasing
+// order in binary64 starting from +0.0.  Chunks in [nchunk, np2) are the
+// tree's zero padding.  grid = (ceil(np2 / chunks per block), B*hkv).
+template <typename IT, int D>
+__global__ __launch_bounds__(256) void k_kmean_partial(const IT* __restrict__ k, int64_t sb, int64_t sh, int64_t sn,
+                                                       int32_t hkv, int32_t N, int32_t np2, double* __restrict__ part) {
+  constexpr int L = D / 8;
+  constexpr int CPB = 256 / L;
+  const int32_t li = threadIdx.x % L;
+  const int32_t t = blockIdx.x * CPB + threadIdx.x / L;
+  const int32_t bg = blockIdx.y;
+  if (t >= np2) return;
   const int32_t b = bg / hkv, g = bg % hkv;
-  double s = 0.0;
+  double s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = 0.0;
   const int32_t n0 = t * 64;
   const int32_t n1 = min(n0 + 64, N);
-  const IT* base = k + b * sb + g * sh + c;
-  for (int32_t n = n0; n < n1; ++n) {
-    float x;
-    if constexpr (sizeof(IT) == 2) x = bf16_to_f32(base[static_cast<int64_t>(n) * sn]);
-    else x = base[static_cast<int64_t>(n) * sn];
-    s += static_cast<double>(x);
+  const IT* base = k + b * sb + g * sh + 8 * li;
+  int32_t n = n0;
+  for (; n + 8 <= n1; n += 8) {
+    float x[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) load8<IT>(base + static_cast<int64_t>(n + r) * sn, x[r]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(x[r][e]);
   }
-  part[(static_cast<int64_t>(bg) * np2 + t) * D + c] = s;
+  for (; n < n1; ++n) {
+    float x[8];
+    load8<IT>(base + static_cast<int64_t>(n) * sn, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] += static_cast<double>(x[e]);
+  }
+  double* dst = part + (static_cast<int64_t>(bg) * np2 + t) * D + 8 * li;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = s[e];
 }
 
-// Pairwise tree over the chunk partials (in place), then one binary64 division
-// by N and rounding to binary32.
-__global__ void k_kmean_final(double* __restrict__ part, int32_t np2, int32_t N, int32_t D, float* __restrict__ mu) {
-  const int32_t bg = blockIdx.x, c = threadIdx.x;
-  if (c >= D) return;
-  double* col = part + static_cast<int64_t>(bg) * np2 * D + c;
-  for (int32_t w = np2; w > 1; w >>= 1)
-    for (int32_t t = 0; t < w / 2; ++t) col[static_cast<int64_t>(t) * D] = col[static_cast<int64_t>(2 * t) * D] + col[static_cast<int64_t>(2 * t + 1) * D];
-  mu[static_cast<int64_t>(bg) * D + c] = static_cast<float>(col[0] / static_cast<double>(N));
+// Pairwise tree over the np2 chunk partials of each channel (left + right at
+// every node, leaves in chunk order), then one binary64 division by N and
+// rounding to binary32.  A block handles 8 channels of one KV head with 32
+// workers per channel: worker w reduces the aligned subtree of leaves
+// [w*Lw, (w+1)*Lw) with a stack (after leaf i the top ctz(i+1) entries are
+// folded, which builds exactly that subtree), then the 32 subtree sums are
+// combined level by level.  Aligned power-of-two subtrees are nodes of the
+// full tree, so the result is the full tree's.  grid = (B*hkv, D/8).
+constexpr int kMeanCh = 8;
+constexpr int kMeanW = 32;
+
+__global__ __launch_bounds__(kMeanCh * kMeanW) void k_kmean_final(const double* __restrict__ part, int32_t np2,
+                                                                  int32_t N, int32_t D, float* __restrict__ mu) {
+  // N <= 2^30 gives np2 <= 2^24, so a worker's subtree has at most 2^19
+  // leaves and its stack at most 20 entries.
+  __shared__ double stack[kMeanCh * kMeanW][24];
+  __shared__ double res[kMeanCh][kMeanW];
+  const int32_t tid = threadIdx.x, cl = tid % kMeanCh, w = tid / kMeanCh;
+  const int32_t c = blockIdx.y * kMeanCh + cl;
+  const int32_t bg = blockIdx.x;
+  const int32_t W = min(np2, kMeanW);
+  const int32_t Lw = np2 / W;
+  double v = 0.0;
+  if (w < W) {
+    const double* col = part + (static_cast<int64_t>(bg) * np2 + static_cast<int64_t>(w) * Lw) * D + c;
+    double* st = stack[tid];
+    int32_t depth = 0;
+    for (int32_t i0 = 0; i0 < Lw; i0 += 8) {
+      double xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = (i0 + e < Lw) ? col[static_cast<int64_t>(i0 + e) * D] : 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (i0 + e < Lw) {
+          double x = xs[e];
+          for (int32_t f = __builtin_ctz(static_cast<uint32_t>(i0 + e + 1)); f > 0; --f) x = st[--depth] + x;
+          st[depth++] = x;
+        }
+      }
+    }
+    v = st[0];
+  }
+  res[cl][w] = v;
+  __syncthreads();
+  for (int32_t m = W; m > 1; m >>= 1) {
+    double x = 0.0;
+    if (w < m / 2) x = res[cl][2 * w] + res[cl][2 * w + 1];
+    __syncthreads();
+    if (w < m / 2) res[cl][w] = x;
+    __syncthreads();
+  }
+  if (w == 0) mu[static_cast<int64_t>(bg) * D + c] = static_cast<float>(res[cl][0] / static_cast<double>(N));
 }
 
 // One row (D channels) held by D/8 lanes, 8 channels per lane: optional
@@ -272,8 +334,10 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq;
   uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv;
   if (a.center) {
-    k_kmean_partial<IT><<<dim3(a.np2, B * hkv), dim3(D), 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, D, a.np2, a.mean_part);
-    k_kmean_final<<<dim3(B * hkv), dim3(D), 0, st>>>(a.mean_part, a.np2, N, D, a.k_mean);
+    constexpr int32_t kChunksPerBlock = 256 / (D / 8);
+    k_kmean_partial<IT, D><<<dim3((a.np2 + kChunksPerBlock - 1) / kChunksPerBlock, B * hkv), dim3(256), 0, st>>>(
+        k, a.ks[0], a.ks[1], a.ks[2], hkv, N, a.np2, a.mean_part);
+    k_kmean_final<<<dim3(B * hkv, D / kMeanCh), dim3(kMeanCh * kMeanW), 0, st>>>(a.mean_part, a.np2, N, D, a.k_mean);
   }
   const dim3 gq((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
   const dim3 gk((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);

@@ -103,6 +103,14 @@ def test_degenerate_lengths(pan, N):
         run_case(pan, w, cond, 256.0, 1, 128, True)
 
 
+def test_mean_key_tree_with_padding(pan):
+    """41 chunks of 64 tokens (the last one ragged): the chunk tree is padded
+    to 64 leaves and split over the reduction's workers."""
+    w = synth.qwen_like(1, 2, 1, 64, seed=245, N=40 * 64 + 17, texts=1)
+    for cond in ("centered", "centered_rotated"):
+        run_case(pan, w, cond, 256.0, 1, 128, True)
+
+
 def test_zero_head_and_strided_input(pan):
     """An all-zero head gets unit scales; a strided [B,N,H,d] view quantises
     exactly like the dense copy."""
