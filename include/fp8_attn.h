@@ -132,6 +132,13 @@ int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
  *   p_dump     device out, uint8 [B,hq,N,N] P~ codes (may be NULL): every key of
  *              every visited block is written (0 for masked keys); keys of
  *              unvisited blocks are left untouched, so zero it first.
+ *   row_hash   device out, uint64 [B,hq,N] (may be NULL): a checksum of the
+ *              row's P~ codes for verification, sum over keys j of
+ *              code_ij * W_j modulo 2^64 (masked keys have code 0), with
+ *              W_j = splitmix64(j) | 1, the (j+1)-th output of a splitmix64
+ *              generator seeded with 0 (Steele, Lea and Flood, OOPSLA 2014).
+ *              It does not depend on the visit order, and the odd weights make
+ *              any single changed code change it.
  *   row_zeros  device out, uint32 [B,hq,N] (may be NULL): number of visible
  *              keys j >= k_sink whose P~ code is 0.
  * Errors: FP8A_ERR_SHAPE also when, with E4M3 operands, one head's codes
@@ -141,8 +148,8 @@ int fp8_attn_fwd(const fp8a_shape* shape, fp8a_dtype qkv_dtype,
                  const void* q, const void* k, const void* v,
                  const float* q_desc, const float* k_desc, const float* v_desc,
                  float softmax_scale, float p_scale, int32_t kv_order, int32_t block_n, int32_t causal,
-                 float* out, float* lse, uint8_t* p_dump, uint32_t* row_zeros, int32_t k_sink,
-                 void* stream);
+                 float* out, float* lse, uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros,
+                 int32_t k_sink, void* stream);
 
 /* Workspace needed by fp8_attn_head_error (bytes). */
 size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* shape, int64_t nrows);

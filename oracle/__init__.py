@@ -31,6 +31,7 @@ not print) is marked "parity unpinned" there.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -280,6 +281,41 @@ def attention_pcast_f32(q, k, v, softmax_scale: float | None = None, p_scale: fl
 
 
 # --------------------------------------------------------------- metrics
+
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, count: int) -> list[int]:
+    """The first `count` outputs of the splitmix64 generator from `seed`
+    (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+    OOPSLA 2014): add the golden-ratio increment to the state, then xor-shift
+    and multiply twice."""
+    out = []
+    state = seed & _M64
+    for _ in range(count):
+        state = (state + 0x9E3779B97F4A7C15) & _M64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+@functools.lru_cache(maxsize=8)
+def key_weights(n: int) -> np.ndarray:
+    """W_j = splitmix64 output j+1 from seed 0, made odd, for keys j < n
+    (cached: do not modify the returned array)."""
+    return np.array([w | 1 for w in splitmix64(0, n)], dtype=np.uint64)
+
+
+def row_hash(p) -> np.ndarray:
+    """Checksum of each row of P~ codes for verification (not part of the
+    method): sum over keys j of code_j * W_j modulo 2^64.  p [..., N] uint8."""
+    p = np.asarray(p)
+    w = key_weights(p.shape[-1])
+    with np.errstate(over="ignore"):
+        return (p.astype(np.uint64) * w).sum(axis=-1, dtype=np.uint64)
+
 
 def head_errors(o, ref) -> np.ndarray:
     """Relative Frobenius error per (batch, head): ||O - R||_F / ||R||_F over

@@ -49,7 +49,8 @@ def _load():
     lib.fp8_attn_prepare_workspace_bytes.restype = sz
     lib.fp8_attn_prepare.argtypes = [sp, ctypes.c_int, vp, vp, vp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fp8_attn_prepare.restype = ctypes.c_int
-    lib.fp8_attn_fwd.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, vp, vp, vp, vp, i32, vp]
+    lib.fp8_attn_fwd.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                 i32, vp]
     lib.fp8_attn_fwd.restype = ctypes.c_int
     lib.fp8_attn_head_error_workspace_bytes.argtypes = [sp, i64]
     lib.fp8_attn_head_error_workspace_bytes.restype = sz
@@ -123,11 +124,11 @@ def fp8_attn_prepare(shape: Shape, q, k, v, flags: int, rot_signs, q8, k8, v8t, 
 
 def fp8_attn_fwd(shape: Shape, qkv_dtype: int, q, k, v, q_desc, k_desc, v_desc, softmax_scale: float,
                  p_scale: float, kv_order: int, block_n: int, causal: int, out, lse=None, p_dump=None,
-                 row_zeros=None, k_sink: int = 0, stream=None) -> None:
+                 row_hash=None, row_zeros=None, k_sink: int = 0, stream=None) -> None:
     rc = _lib.fp8_attn_fwd(ctypes.byref(shape), int(qkv_dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(q_desc),
                            _ptr(k_desc), _ptr(v_desc), float(softmax_scale), float(p_scale), int(kv_order),
-                           int(block_n), int(causal), _ptr(out), _ptr(lse), _ptr(p_dump), _ptr(row_zeros),
-                           int(k_sink), _stream(stream))
+                           int(block_n), int(causal), _ptr(out), _ptr(lse), _ptr(p_dump), _ptr(row_hash),
+                           _ptr(row_zeros), int(k_sink), _stream(stream))
     if rc != 0:
         raise Fp8AttnError(rc, "fp8_attn_fwd")
 

@@ -143,7 +143,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
 int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const void* k, const void* v,
                  const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
                  float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out, float* lse,
-                 uint8_t* p_dump, uint32_t* row_zeros, int32_t k_sink, void* stream) {
+                 uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink, void* stream) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32) return FP8A_ERR_UNSUPPORTED;
@@ -171,7 +171,7 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
     fp8a::PcastParams p;
     memset(&p, 0, sizeof p);
     p.q = static_cast<const float*>(q); p.k = static_cast<const float*>(k); p.v = static_cast<const float*>(v);
-    p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_zeros = row_zeros;
+    p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_hash = row_hash; p.row_zeros = row_zeros;
     p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.block_n = block_n;
     p.kv_order = kv_order; p.causal = causal; p.k_sink = k_sink;
     p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
@@ -181,7 +181,7 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
   memset(&p, 0, sizeof p);
   p.q8 = static_cast<const uint8_t*>(q); p.k8 = static_cast<const uint8_t*>(k); p.v8t = static_cast<const uint8_t*>(v);
   p.q_desc = q_desc; p.k_desc = k_desc; p.v_desc = v_desc;
-  p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_zeros = row_zeros;
+  p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_hash = row_hash; p.row_zeros = row_zeros;
   p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.Np = fp8_attn_padded_seqlen(s->seqlen);
   p.n_qtiles = p.Np / 128; p.kv_order = kv_order; p.k_sink = k_sink;
   p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
@@ -193,7 +193,7 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
     p.fix0 = rn32_exp2(x0);
     p.fix1 = rn32_exp2(x1);
   }
-  const bool dump = p_dump != nullptr || row_zeros != nullptr;
+  const bool dump = p_dump != nullptr || row_hash != nullptr || row_zeros != nullptr;
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));
 }
 

@@ -15,6 +15,7 @@ struct FwdParams {
   float* out;             // [B,hq,N,D]
   float* lse;             // [B,hq,N] or null
   uint8_t* p_dump;        // [B,hq,N,N] or null
+  uint64_t* row_hash;     // [B,hq,N] or null
   uint32_t* row_zeros;    // [B,hq,N] or null
   int32_t B, hq, hkv, N, Np, n_qtiles, kv_order, k_sink;
   float ls2;              // RN32(softmax_scale * log2 e)
@@ -32,6 +33,7 @@ struct PcastParams {
   float* out;
   float* lse;
   uint8_t* p_dump;
+  uint64_t* row_hash;
   uint32_t* row_zeros;
   int32_t B, hq, hkv, N, block_n, kv_order, causal, k_sink;
   float ls2, S, inv_S;

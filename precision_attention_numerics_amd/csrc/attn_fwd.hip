@@ -144,6 +144,16 @@ __device__ __forceinline__ v8i lds_read_pair(const uint8_t* p0, const uint8_t* p
   return r;
 }
 
+// Weight of key j in the P~ row checksum: splitmix64's (j+1)-th output from
+// seed 0 (Steele, Lea and Flood, OOPSLA 2014), made odd so that every code
+// change moves the sum.
+__device__ __forceinline__ uint64_t key_weight(int j) {
+  uint64_t z = static_cast<uint64_t>(j + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (z ^ (z >> 31)) | 1ull;
+}
+
 // Maximum that propagates NaN (v_maximum3_f32 on gfx950; unlike fmaxf it
 // needs no quieting of its inputs).  Scores are finite or -inf here.
 __device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -171,11 +181,13 @@ __device__ __forceinline__ float column_sum(float v) {
 // values (only run when a wave holds such an x).  MASK zeroes invisible keys.
 template <int T, bool MASK, bool FIX, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T], float& lpart, uint32_t& zpart,
-                                                               const int lim, const int i, const int jb, const int N,
-                                                               const FwdParams& p, uint8_t* __restrict__ dump_row) {
+                                                               uint64_t& hpart, const int lim, const int i, const int jb,
+                                                               const int N, const FwdParams& p,
+                                                               uint8_t* __restrict__ dump_row) {
   v8i out;
   float part[T];
   uint32_t zeros = 0;
+  uint64_t hsum = 0;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     float pr[4];
@@ -209,6 +221,7 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
         const bool vis = (j < N) && (!CAUSAL || j <= i);
         const uint32_t code = (w >> (8 * r)) & 0xFFu;
         if (vis && j >= p.k_sink && code == 0u) ++zeros;
+        if (code != 0u) hsum += static_cast<uint64_t>(code) * key_weight(j);
         if (dump_row && i < N && j < N) dump_row[j] = static_cast<uint8_t>(code);
       }
     }
@@ -220,6 +233,7 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
     for (int t = 0; t < w; ++t) part[t] = part[t] + part[t + w];
   lpart = part[0];
   zpart = zeros;
+  hpart = hsum;
 #pragma unroll
   for (int t = T; t < 8; ++t) out[t] = 0;
   return out;
@@ -232,7 +246,8 @@ template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], const float c, float& ms, float& mcp,
                                                                   float& lsum, v4f (&oacc)[D / 16], const int i,
                                                                   const int jb, const int N, const FwdParams& p,
-                                                                  uint32_t& zeros, uint8_t* __restrict__ dump_row) {
+                                                                  uint32_t& zeros, uint64_t& hash,
+                                                                  uint8_t* __restrict__ dump_row) {
   // key jb + k is visible iff k < lim (k = 4t + r): one compare per key
   const int lim = min(N, CAUSAL ? i + 1 : N) - jb;
   if constexpr (MASK) {
@@ -285,13 +300,15 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
   }
   float lpart;
   uint32_t zpart;
+  uint64_t hpart;
   v8i out;
   if (__builtin_expect(fix, 0))
-    out = cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
+    out = cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
   else
-    out = cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, lpart, zpart, lim, i, jb, N, p, dump_row);
+    out = cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
+  hash += hpart;
   return out;
 }
 
@@ -365,10 +382,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   // ---- running state per query tile (replicated over the 4 lane groups)
   float ms[QT], mcp[QT], lsum[QT];
   uint32_t zeros[QT];
+  uint64_t hash[QT];
   v4f oacc[QT][D / 16];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    ms[qt] = -INFINITY; mcp[qt] = -INFINITY; lsum[qt] = 0.0f; zeros[qt] = 0;
+    ms[qt] = -INFINITY; mcp[qt] = -INFINITY; lsum[qt] = 0.0f; zeros[qt] = 0; hash[qt] = 0;
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) oacc[qt][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -422,10 +440,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       if constexpr (DUMP) drow = p.p_dump ? p.p_dump + (static_cast<int64_t>(bh) * N + i) * N : nullptr;
       if (DUMP || need_mask)
         pop[qt] = softmax_tile<D, T, true, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
-                                                              j0 + KPL * lg, N, p, zeros[qt], drow);
+                                                              j0 + KPL * lg, N, p, zeros[qt], hash[qt], drow);
       else
         pop[qt] = softmax_tile<D, T, false, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
-                                                               j0 + KPL * lg, N, p, zeros[qt], drow);
+                                                               j0 + KPL * lg, N, p, zeros[qt], hash[qt], drow);
     }
 
     // ---- O^T += V^T P^T
@@ -462,6 +480,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       z += __shfl_xor(z, 16, kWave);
       z += __shfl_xor(z, 32, kWave);
       if (p.row_zeros && lg == 0 && i < N) p.row_zeros[static_cast<int64_t>(bh) * N + i] = z;
+      unsigned long long hs = hash[qt];
+      hs += __shfl_xor(hs, 16, kWave);
+      hs += __shfl_xor(hs, 32, kWave);
+      if (p.row_hash && lg == 0 && i < N) p.row_hash[static_cast<int64_t>(bh) * N + i] = hs;
     }
   }
 }
@@ -490,6 +512,7 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
   const int J = (nvis - 1) / BC;
   float ms = -INFINITY, mcp = -INFINITY, l = 0.0f;
   uint32_t zeros = 0;
+  uint64_t hash = 0;
   for (int t = 0; t <= J; ++t) {
     const int blk = p.kv_order ? J - t : t;
     const int ja = blk * BC, jb = min((blk + 1) * BC, nvis);
@@ -519,6 +542,7 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
       const float pt = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(code), 0);
       l = l + pv;
       if (j >= p.k_sink && code == 0u) ++zeros;
+      if (code != 0u) hash += static_cast<uint64_t>(code) * key_weight(j);
       if (p.p_dump) p.p_dump[(static_cast<int64_t>(bh) * N + i) * N + j] = static_cast<uint8_t>(code);
 #pragma unroll
       for (int cc = 0; cc < D; ++cc) acc[cc] = acc[cc] + pt * V[static_cast<int64_t>(j) * D + cc];
@@ -532,6 +556,7 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
   for (int cc = 0; cc < D; ++cc) o[cc] = acc[cc] * f;
   if (p.lse) p.lse[static_cast<int64_t>(bh) * N + i] = (mcp + __log2f(l)) * 0.69314718055994531f;
   if (p.row_zeros) p.row_zeros[static_cast<int64_t>(bh) * N + i] = zeros;
+  if (p.row_hash) p.row_hash[static_cast<int64_t>(bh) * N + i] = hash;
 }
 
 // ------------------------------------------------------------------ launch

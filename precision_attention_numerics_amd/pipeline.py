@@ -59,25 +59,26 @@ class AttnPipeline:
 
     def fwd(self, prep: Prepared, p_scale: float = 256.0, kv_order: int = 1, block_n: int = 128,
             causal: bool = True, softmax_scale: float | None = None, out=None, lse=None, p_dump=None,
-            row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
+            row_hash=None, row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.d)
         if out is None:
             out = torch.empty((self.B, self.hq, self.N, self.d), dtype=torch.float32, device=self.device)
         _abi.fp8_attn_fwd(self.shape, _abi.FP8A_E4M3, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
-                          prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse, p_dump,
-                          row_zeros, k_sink, stream)
+                          prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse=lse,
+                          p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros, k_sink=k_sink, stream=stream)
         return out
 
     def fwd_f32(self, q, k, v, p_scale: float = 256.0, kv_order: int = 0, block_n: int = 128,
                 causal: bool = False, softmax_scale: float | None = None, out=None, lse=None, p_dump=None,
-                row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
+                row_hash=None, row_zeros=None, k_sink: int = 0, stream=None) -> torch.Tensor:
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(self.d)
         if out is None:
             out = torch.empty((self.B, self.hq, self.N, self.d), dtype=torch.float32, device=self.device)
         _abi.fp8_attn_fwd(self.shape, _abi.FP8A_F32, q, k, v, None, None, None, softmax_scale, p_scale, kv_order,
-                          block_n, int(causal), out, lse, p_dump, row_zeros, k_sink, stream)
+                          block_n, int(causal), out, lse=lse, p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros,
+                          k_sink=k_sink, stream=stream)
         return out
 
     def head_error(self, out, ref, rows=None, rel_err=None, stream=None) -> torch.Tensor:

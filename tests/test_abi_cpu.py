@@ -86,7 +86,7 @@ def _fwd(abi, shape, **kw):
     a.update(kw)
     return abi._lib.fp8_attn_fwd(ctypes.byref(shape), a["dtype"], FAKE, FAKE, FAKE, a["desc"], a["desc"], a["desc"],
                                  a["scale"], a["S"], a["order"], a["bn"], a["causal"], a["out"], None, None, None,
-                                 a["k_sink"], None)
+                                 None, a["k_sink"], None)
 
 
 def test_prepare_rejects(abi):

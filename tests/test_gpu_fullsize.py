@@ -97,12 +97,13 @@ def test_long_context_full_size(pan, workloads, cond):
     sub = pan.AttnPipeline(1, 1, 1, N, d)
     pd = torch.empty((1, 1, N, N), dtype=torch.uint8, device="cuda")
     rz = torch.empty((1, 1, N), dtype=torch.int32, device="cuda")
+    rh = torch.empty((1, 1, N), dtype=torch.int64, device="cuda")
     for h in range(hq):
         g = h // grp
         pd.zero_()
         rz.zero_()
-        oh = sub.fwd(_head_view(pan, gp, 0, 1, h, h + 1, g, g + 1, hq, hkv), p_dump=pd, row_zeros=rz,
-                     k_sink=K_SINK, **kw)
+        oh = sub.fwd(_head_view(pan, gp, 0, 1, h, h + 1, g, g + 1, hq, hkv), p_dump=pd, row_hash=rh,
+                     row_zeros=rz, k_sink=K_SINK, **kw)
         torch.cuda.synchronize()
         assert torch.equal(oh[0, 0], out[0, h]), f"head {h}: single-head dump run differs from the full run"
         P = pd[0, 0][rows_dev].cpu().numpy()
@@ -110,6 +111,8 @@ def test_long_context_full_size(pan, workloads, cond):
         assert nbad == 0, f"head {h}: {nbad} P codes differ, first at {np.argwhere(P != ref.p[0, h])[:5]}"
         Z = rz[0, 0][rows_dev].cpu().numpy().astype(np.uint32)
         assert np.array_equal(Z, ref.row_zeros[0, h]), f"head {h}: zero counts differ"
+        Hs = rh[0, 0][rows_dev].cpu().numpy().view(np.uint64)
+        assert np.array_equal(Hs, oracle.row_hash(ref.p[0, h])), f"head {h}: row checksums differ"
     print(f"[fullsize] {cond}: P codes of {rows.size} rows x {hq} heads bit-exact", flush=True)
 
 
@@ -128,6 +131,7 @@ def test_qwen_stack_full_shape(pan, workloads, model, cond):
     sub = pan.AttnPipeline(texts, hq, hkv, N, d)
     pd = torch.empty((texts, hq, N, N), dtype=torch.uint8, device="cuda")
     rz = torch.empty((texts, hq, N), dtype=torch.int32, device="cuda")
+    rh = torch.empty((texts, hq, N), dtype=torch.int64, device="cuda")
     worst = 0.0
     t0 = time.time()
     for layer in range(layers):
@@ -141,14 +145,15 @@ def test_qwen_stack_full_shape(pan, workloads, model, cond):
         assert max_head_rel(o, ref.out) <= TOL_O, errs.max()
         pd.zero_()
         rz.zero_()
-        ol_dev = sub.fwd(_head_view(pan, gp, b0, b1, 0, hq, 0, hkv, hq, hkv), p_dump=pd, row_zeros=rz,
-                         k_sink=K_SINK, **kw)
+        ol_dev = sub.fwd(_head_view(pan, gp, b0, b1, 0, hq, 0, hkv, hq, hkv), p_dump=pd, row_hash=rh,
+                         row_zeros=rz, k_sink=K_SINK, **kw)
         torch.cuda.synchronize()
         assert torch.equal(ol_dev, out[b0:b1]), f"layer {layer}: dump run differs from the full run"
         P = pd.cpu().numpy()
         nbad = p_mismatch(P, ref.p)
         assert nbad == 0, f"layer {layer}: {nbad} P codes differ, first at {np.argwhere(P != ref.p)[:5]}"
         assert np.array_equal(rz.cpu().numpy().astype(np.uint32), ref.row_zeros), f"layer {layer}: zero counts"
+        assert np.array_equal(rh.cpu().numpy().view(np.uint64), oracle.row_hash(ref.p)), f"layer {layer}: checksums"
         worst = max(worst, float(errs.max()))
         if layer % 8 == 0:
             print(f"[fullsize] {w.name} {cond} layer {layer}: P bit-exact ({time.time() - t:.1f}s)", flush=True)

@@ -37,7 +37,9 @@ def run_case(pan, w, cond, p_scale, kv_order, block_n, causal, rows=None, check_
     compare_prepared(gp, op, N, flags["center"])
     pd = torch.zeros((B, hq, N, N), dtype=torch.uint8, device="cuda")
     rz = torch.zeros((B, hq, N), dtype=torch.int32, device="cuda")
-    out = pipe.fwd(gp, p_scale=p_scale, kv_order=kv_order, block_n=block_n, causal=causal, p_dump=pd, row_zeros=rz, k_sink=4)
+    rh = torch.zeros((B, hq, N), dtype=torch.int64, device="cuda")
+    out = pipe.fwd(gp, p_scale=p_scale, kv_order=kv_order, block_n=block_n, causal=causal, p_dump=pd, row_hash=rh,
+                   row_zeros=rz, k_sink=4)
     out_nodump = pipe.fwd(gp, p_scale=p_scale, kv_order=kv_order, block_n=block_n, causal=causal)
     torch.cuda.synchronize()
     ref = oracle.attention_fp8(op, p_scale=p_scale, kv_order=kv_order, block_n=block_n, causal=causal,
@@ -46,11 +48,13 @@ def run_case(pan, w, cond, p_scale, kv_order, block_n, causal, rows=None, check_
     assert np.array_equal(o, out_nodump.cpu().numpy()), "dump and timed variants differ"
     P = pd.cpu().numpy()
     Z = rz.cpu().numpy().astype(np.uint32)
+    H = rh.cpu().numpy().view(np.uint64)
     if rows is not None:
-        o, P, Z = o[:, :, rows], P[:, :, rows], Z[:, :, rows]
+        o, P, Z, H = o[:, :, rows], P[:, :, rows], Z[:, :, rows], H[:, :, rows]
     nbad = p_mismatch(P, ref.p)
     assert nbad == 0, f"{nbad} P codes differ, first at {np.argwhere(P != ref.p)[:5]}"
     assert np.array_equal(Z, ref.row_zeros)
+    assert np.array_equal(H, oracle.row_hash(ref.p)), "P row checksums differ"
     err = max_head_rel(o, ref.out)
     assert err <= TOL_O, err
     if check_ideal:
@@ -154,14 +158,16 @@ def test_pcast_sweep_points(pan, delta):
             print(f"pcast delta={delta} order={order} S={S}", flush=True)
             pd = torch.zeros((1, 1, 4096, 4096), dtype=torch.uint8, device="cuda")
             rz = torch.zeros((1, 1, 4096), dtype=torch.int32, device="cuda")
+            rh = torch.zeros((1, 1, 4096), dtype=torch.int64, device="cuda")
             out = pipe.fwd_f32(q, k, v, p_scale=S, kv_order=order, block_n=128, causal=False, p_dump=pd,
-                               row_zeros=rz, k_sink=4)
+                               row_hash=rh, row_zeros=rz, k_sink=4)
             torch.cuda.synchronize()
             ref = oracle.attention_pcast_f32(w.q, w.k, w.v, p_scale=S, kv_order=order, block_n=128, causal=False,
                                              rows=rows, want_p=True, k_sink=4)
             P = pd.cpu().numpy()[:, :, rows]
             assert p_mismatch(P, ref.p) == 0
             assert np.array_equal(rz.cpu().numpy()[:, :, rows].astype(np.uint32), ref.row_zeros)
+            assert np.array_equal(rh.cpu().numpy().view(np.uint64)[:, :, rows], oracle.row_hash(ref.p))
             assert max_head_rel(out.cpu().numpy()[:, :, rows], ref.out) <= TOL_O
 
 
