@@ -417,24 +417,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
     const uint8_t* kt = klds + cur;
     const uint8_t* vt = vlds + cur;
 
-    // ---- per 16-row query tile: S^T = K Q^T, then the online softmax and the
-    // P cast; the lane ends up holding query n16 and keys j0 + KPL*lg + 4t + r.
+    // ---- S^T = K Q^T for both 16-row query tiles from one LDS read of each K
+    // tile, then per query tile the online softmax and the P cast; the lane
+    // ends up holding query n16 and keys j0 + KPL*lg + 4t + r.
     const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wrow0);
     v8i pop[QT];
+    v4f sall[QT][T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      v8i a;
+      if (has_k) {
+        a = lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = 0;
+      }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) sall[qt][t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      v4f sacc[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        v8i a;
-        if (has_k) {
-          a = lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = 0;
-        }
-        sacc[t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-      }
+      v4f (&sacc)[T] = sall[qt];
       const int i = wrow0 + qt * 16 + n16;
       uint8_t* drow = nullptr;
       if constexpr (DUMP) drow = p.p_dump ? p.p_dump + (static_cast<int64_t>(bh) * N + i) * N : nullptr;

@@ -141,6 +141,36 @@ __global__ __launch_bounds__(kMeanCh * kMeanW) void k_kmean_final(const double* 
   if (w == 0) mu[static_cast<int64_t>(bg) * D + c] = static_cast<float>(res[cl][0] / static_cast<double>(N));
 }
 
+// Value of lane (lane ^ M) within a group of 16 lanes (M = 1, 2, 4, 8), by DPP
+// (no LDS): quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2, row_half_mirror
+// then quad_perm [3,2,1,0] for 4 (7 - ((i^3) & 7) = (i ^ 4) & 7), row_ror:8
+// for 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor16(float v) {
+  if constexpr (M == 1) return dpp_mov<0xB1>(v);
+  else if constexpr (M == 2) return dpp_mov<0x4E>(v);
+  else if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));
+  else return dpp_mov<0x128>(v);
+}
+
+// Butterfly stage h = 8*M across the lanes of a row: the lower lane keeps
+// x + y, the upper y - x (y = partner's value), written as y + (+-x), which is
+// the same binary32 operation.
+template <int M>
+__device__ __forceinline__ void cross_stage(float x[8], int li) {
+  const uint32_t flip = (li & M) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = lane_xor16<M>(x[e]);
+    x[e] = y + __uint_as_float(__float_as_uint(x[e]) ^ flip);
+  }
+}
+
 // One row (D channels) held by D/8 lanes, 8 channels per lane: optional
 // centring, sign flip and unnormalised Sylvester Walsh-Hadamard transform in
 // the stage order h = 1, 2, ..., D/2.
@@ -165,20 +195,16 @@ __device__ __forceinline__ void transform_row(float x[8], int li, const float* _
         }
       }
     }
-#pragma unroll
-    for (int lh = 1; lh < D / 8; lh <<= 1) {
-      const bool upper = (li & lh) != 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float y = wave_xor(x[e], lh);
-        x[e] = upper ? (y - x[e]) : (x[e] + y);
-      }
-    }
+    if constexpr (D / 8 > 1) cross_stage<1>(x, li);
+    if constexpr (D / 8 > 2) cross_stage<2>(x, li);
+    if constexpr (D / 8 > 4) cross_stage<4>(x, li);
+    if constexpr (D / 8 > 8) cross_stage<8>(x, li);
   }
 }
 
 constexpr int kPrepThreads = 256;
 constexpr int kRowsPerBlock = 256;
+constexpr int kRowsInFlight = 4;
 
 // Per-head max |x| of the transformed rows.  grid = (ceil(N / 256), B*H).
 template <typename IT, int D, bool ROT, bool CENTER>
@@ -195,20 +221,34 @@ __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x,
   float m = 0.0f;
   bool bad = false;
   const int n_begin = blockIdx.x * kRowsPerBlock;
-  for (int r = rl; r < kRowsPerBlock; r += RPI) {
-    const int n = n_begin + r;
-    if (n >= N) break;
-    float v[8];
-    load8<IT>(base + static_cast<int64_t>(n) * sn, v);
+  // kRowsInFlight rows per lane group per step, loaded before any is
+  // transformed.  Rows past N are not loaded and not counted; the L lanes of a
+  // row share r, so the lane exchanges of a row always run on all its lanes.
+  for (int r0 = rl; r0 < kRowsPerBlock; r0 += kRowsInFlight * RPI) {
+    float v[kRowsInFlight][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bad |= !__builtin_isfinite(v[e]);
-    transform_row<D, ROT, CENTER>(v, li, mu, signs);
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int n = n_begin + r0 + u * RPI;
+      if (r0 + u * RPI < kRowsPerBlock && n < N) {
+        load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int n = n_begin + r0 + u * RPI;
+      const bool live = r0 + u * RPI < kRowsPerBlock && n < N;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bad |= live && !__builtin_isfinite(v[u][e]);
+      transform_row<D, ROT, CENTER>(v[u], li, mu, signs);
+      if (live) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[u][e]));
+      }
+    }
   }
-  // Every lane of a row group takes part in the shuffles above, so rows past N
-  // must be skipped by the whole group together: the loop bound is uniform
-  // across the L lanes of a row (they share r).
 #pragma unroll
   for (int s = 1; s < kWave; s <<= 1) m = __builtin_fmaxf(m, wave_xor(m, s));
   __shared__ float red[kPrepThreads / kWave];
@@ -252,22 +292,37 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
   const IT* base = x + b * sb + h * sh + 8 * li;
   uint8_t* out = codes + static_cast<int64_t>(bh) * Np * D + 8 * li;
   const int n_begin = blockIdx.x * kRowsPerBlock;
-  for (int r = rl; r < kRowsPerBlock; r += RPI) {
-    const int n = n_begin + r;
-    if (n >= Np) break;
-    uint2 w = make_uint2(0u, 0u);
-    if (n < N) {
-      float v[8];
-      load8<IT>(base + static_cast<int64_t>(n) * sn, v);
-      transform_row<D, ROT, CENTER>(v, li, mu, signs);
-      uint32_t lo = 0, hi = 0;
-      lo = e4m3_pack2<false>(v[0] * inv, v[1] * inv, lo);
-      lo = e4m3_pack2<true>(v[2] * inv, v[3] * inv, lo);
-      hi = e4m3_pack2<false>(v[4] * inv, v[5] * inv, hi);
-      hi = e4m3_pack2<true>(v[6] * inv, v[7] * inv, hi);
-      w = make_uint2(lo, hi);
+  // kRowsInFlight rows per lane group per step, loaded before any is
+  // transformed (the L lanes of a row share r, so its lane exchanges always run
+  // on all of them).
+  for (int r0 = rl; r0 < kRowsPerBlock; r0 += kRowsInFlight * RPI) {
+    float v[kRowsInFlight][8];
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int n = n_begin + r0 + u * RPI;
+      if (r0 + u * RPI < kRowsPerBlock && n < N) {
+        load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+      }
     }
-    *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      const int n = n_begin + r0 + u * RPI;
+      transform_row<D, ROT, CENTER>(v[u], li, mu, signs);
+      uint2 w = make_uint2(0u, 0u);
+      if (n < N) {
+        uint32_t lo = 0, hi = 0;
+        lo = e4m3_pack2<false>(v[u][0] * inv, v[u][1] * inv, lo);
+        lo = e4m3_pack2<true>(v[u][2] * inv, v[u][3] * inv, lo);
+        hi = e4m3_pack2<false>(v[u][4] * inv, v[u][5] * inv, hi);
+        hi = e4m3_pack2<true>(v[u][6] * inv, v[u][7] * inv, hi);
+        w = make_uint2(lo, hi);
+      }
+      // rows in [N, Np) are written as zero codes
+      if (r0 + u * RPI < kRowsPerBlock && n < Np) *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
+    }
   }
 }
 
