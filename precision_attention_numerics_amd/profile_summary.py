@@ -7,7 +7,7 @@ sha256 of the kernel source they were measured on)
 
 PROFDIR holds the sub-directories written by these commands (run from /tmp,
 TMPDIR=/tmp, R = repository root):
-  trace: rocprofv3 --kernel-trace --stats -S --output-format csv -d PROFDIR/trace -o trace -- python3 R/bench.py --no-cpu-baseline --steps 5 --warmup 2
+  trace: rocprofv3 --kernel-trace --stats -S --output-format csv -d PROFDIR/trace -o trace -- python3 R/bench.py --no-cpu-baseline --steps 20 --warmup 5
   fetch: rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROFDIR/fetch -o fetch -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
   write: rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROFDIR/write -o write -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
   sq:    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE --output-format csv -d PROFDIR/sq -o sq -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
@@ -39,8 +39,22 @@ def counters(path: str):
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
+def dispatch_median_us(d: str) -> dict:
+    """Median duration per kernel over its dispatches (the average includes the
+    first launches, which run while the clocks ramp up)."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(d, "trace", "trace_kernel_trace.csv"))):
+        per[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for k, v in per.items():
+        v = sorted(v)
+        out[k] = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return out
+
+
 def main(d: str):
     stats = list(csv.DictReader(open(os.path.join(d, "trace", "trace_kernel_stats.csv"))))
+    med = dispatch_median_us(d)
     fetch = counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
     write = counters(os.path.join(d, "write", "write_counter_collection.csv"))
     sq = counters(os.path.join(d, "sq", "sq_counter_collection.csv"))
@@ -50,8 +64,8 @@ def main(d: str):
     cw = [v for (k, c), v in copyw.items() if c == "WRITE_SIZE" and "elementwise" in k]
     f_scale = COPY_BYTES / (max(cf) * 1024) if cf else float("nan")
     w_scale = COPY_BYTES / (max(cw) * 1024) if cw else float("nan")
-    print("| kernel | calls | avg us | HBM read MB/launch | HBM write MB/launch |")
-    print("|---|---|---|---|---|")
+    print("| kernel | calls | avg us | median us | HBM read MB/launch | HBM write MB/launch |")
+    print("|---|---|---|---|---|---|")
     for r in stats:
         k = short(r["Name"])
         if not any(x in k for x in KERNELS):
@@ -60,7 +74,7 @@ def main(d: str):
         ws = write.get((k, "WRITE_SIZE"))
         rd = f"{fs * 1024 * f_scale / 1e6:.1f}" if fs is not None else "-"
         wr = f"{ws * 1024 * w_scale / 1e6:.1f}" if ws is not None else "-"
-        print(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {rd} | {wr} |")
+        print(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med.get(k, float('nan')):.1f} | {rd} | {wr} |")
     print(f"\ncounter scale from the plain 1 GiB copy: FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}\n")
     att = [k for (k, c) in sq if "k_attn_fwd" in k]
     for k in sorted(set(att)):
