@@ -43,6 +43,8 @@ _lib = None
 
 ROTATE = 1
 CENTER = 2
+TILE = 4
+TILE_TOKENS = 128
 SCORE_MODES = {"mfma": 0, "exact": 1}
 
 _c_f32p = ctypes.POINTER(ctypes.c_float)
@@ -76,6 +78,7 @@ def _load():
                                       _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
                                       _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int]
+    lib.orc_attention_fp8_tiles.argtypes = lib.orc_attention_fp8.argtypes
     lib.orc_attention_pcast_f32.argtypes = [_c_f32p, _c_f32p, _c_f32p,
                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
@@ -195,10 +198,14 @@ class Prepared:
     k_desc: np.ndarray
     v_desc: np.ndarray
     k_mean: np.ndarray | None
+    tiles: bool = False     # q_desc [B,Hq,T] / k_desc [B,Hkv,T] per 128-token tile
 
 
-def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None) -> Prepared:
-    """Quantisation prologue on binary32 operands (BF16 widened exactly)."""
+def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, tiles: bool = False) -> Prepared:
+    """Quantisation prologue on binary32 operands (BF16 widened exactly).
+    tiles: one Q/K scale per 128-token tile instead of per (batch, head) (the
+    earlier emulator's granularity, attention-numerics project page, second
+    section); V keeps per-head scales."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     v = np.ascontiguousarray(v, dtype=np.float32)
@@ -208,15 +215,19 @@ def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None) -> 
     q8 = np.empty(q.shape, np.uint8)
     k8 = np.empty(k.shape, np.uint8)
     v8 = np.empty(v.shape, np.uint8)
-    qd = np.empty(B * Hq, np.float32)
-    kd = np.empty(B * Hkv, np.float32)
+    T = (N + TILE_TOKENS - 1) // TILE_TOKENS if tiles else 1
+    qd = np.empty(B * Hq * T, np.float32)
+    kd = np.empty(B * Hkv * T, np.float32)
     vd = np.empty(B * Hkv, np.float32)
     km = np.empty(B * Hkv * d, np.float32) if center else None
-    flags = (ROTATE if rotate else 0) | (CENTER if center else 0)
+    flags = (ROTATE if rotate else 0) | (CENTER if center else 0) | (TILE if tiles else 0)
     rc = _load().orc_prepare(_p(q, _c_f32p), _p(k, _c_f32p), _p(v, _c_f32p), B, Hq, Hkv, N, d, flags,
                              _p(s, _c_i8p), _p(q8, _c_u8p), _p(k8, _c_u8p), _p(v8, _c_u8p),
                              _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p), _p(km, _c_f32p))
     _check(rc, "prepare")
+    if tiles:
+        return Prepared(q8, k8, v8, qd.reshape(B, Hq, T), kd.reshape(B, Hkv, T), vd.reshape(B, Hkv),
+                        None if km is None else km.reshape(B, Hkv, d), True)
     return Prepared(q8, k8, v8, qd.reshape(B, Hq), kd.reshape(B, Hkv), vd.reshape(B, Hkv),
                     None if km is None else km.reshape(B, Hkv, d))
 
@@ -232,7 +243,9 @@ def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: f
                   kv_order: int = 0, block_n: int = 128, causal: bool = True, rows=None,
                   want_p: bool = False, k_sink: int = 0, score_mode: str = "mfma",
                   nthreads: int | None = None) -> LoopResult:
-    """Online-softmax main loop on E4M3 codes.  kv_order 0 = forward, 1 = reverse."""
+    """Online-softmax main loop on E4M3 codes.  kv_order 0 = forward, 1 = reverse.
+    With per-tile descales (prep.tiles) the logit factor is formed per block
+    and the running max kept in scaled units (orc_attention_fp8_tiles)."""
     B, Hq, N, d = prep.q8.shape
     Hkv = prep.k8.shape[1]
     if softmax_scale is None:
@@ -244,12 +257,13 @@ def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: f
     qd = np.ascontiguousarray(prep.q_desc, np.float32)
     kd = np.ascontiguousarray(prep.k_desc, np.float32)
     vd = np.ascontiguousarray(prep.v_desc, np.float32)
-    rc = _load().orc_attention_fp8(_p(prep.q8, _c_u8p), _p(prep.k8, _c_u8p), _p(prep.v8, _c_u8p),
-                                   _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p),
-                                   B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale), int(kv_order),
-                                   int(block_n), int(causal), _p(r, _c_i32p), nrows, _p(out, _c_f32p),
-                                   _p(p, _c_u8p), _p(z, _c_u32p), int(k_sink), SCORE_MODES[score_mode],
-                                   _threads(nthreads))
+    fn = _load().orc_attention_fp8_tiles if prep.tiles else _load().orc_attention_fp8
+    rc = fn(_p(prep.q8, _c_u8p), _p(prep.k8, _c_u8p), _p(prep.v8, _c_u8p),
+            _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p),
+            B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale), int(kv_order),
+            int(block_n), int(causal), _p(r, _c_i32p), nrows, _p(out, _c_f32p),
+            _p(p, _c_u8p), _p(z, _c_u32p), int(k_sink), SCORE_MODES[score_mode],
+            _threads(nthreads))
     _check(rc, "attention_fp8")
     return LoopResult(out, p, z)
 

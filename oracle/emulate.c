@@ -71,6 +71,9 @@ int orc_prepare(const float* q, const float* k, const float* v,
   if (!q || !k || !v || !q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc) return -1;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv || (d & (d - 1))) return -1;
   int rotate = (flags & ORC_ROTATE) != 0, center = (flags & ORC_CENTER) != 0;
+  int tiled = (flags & ORC_TILE) != 0;
+  /* scale groups: the whole sequence, or 128-token tiles */
+  int64_t span = tiled ? ORC_TILE_TOKENS : N, ngroup = (N + span - 1) / span;
   if (rotate && !signs) return -1;
   int64_t nchunk = (N + 63) / 64, np2 = 1;
   while (np2 < nchunk) np2 <<= 1;
@@ -80,35 +83,41 @@ int orc_prepare(const float* q, const float* k, const float* v,
   float* buf = (float*)malloc(sizeof(float) * (size_t)(N * d));
   if (!part || !row || !mu || !buf) { free(part); free(row); free(mu); free(buf); return -3; }
 
-  /* Q: rotate, per-head amax, quantise. */
+  /* Q: rotate, amax per scale group, quantise. */
   for (int64_t bh = 0; bh < B * Hq; ++bh) {
     const float* src = q + bh * N * d;
-    float A = 0.0f;
     for (int64_t n = 0; n < N; ++n) {
       memcpy(buf + n * d, src + n * d, sizeof(float) * (size_t)d);
       if (rotate) orc_fwht_row(buf + n * d, signs, d);
-      for (int64_t c = 0; c < d; ++c) { float a = fabsf(buf[n * d + c]); if (a > A) A = a; }
     }
-    float inv, desc;
-    scales_from_amax(A, rotate, d, &inv, &desc);
-    q_desc[bh] = desc;
-    for (int64_t e = 0; e < N * d; ++e) q8[bh * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+    for (int64_t t = 0; t < ngroup; ++t) {
+      int64_t e0 = t * span * d, e1 = ((t + 1) * span < N ? (t + 1) * span : N) * d;
+      float A = 0.0f;
+      for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
+      float inv, desc;
+      scales_from_amax(A, rotate, d, &inv, &desc);
+      q_desc[bh * ngroup + t] = desc;
+      for (int64_t e = e0; e < e1; ++e) q8[bh * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+    }
   }
   /* K: centre, rotate, amax, quantise.  V: amax, quantise (never rotated). */
   for (int64_t bg = 0; bg < B * Hkv; ++bg) {
     const float* src = k + bg * N * d;
     for (int64_t c = 0; c < d; ++c) mu[c] = center ? column_mean(src, N, d, c, part) : 0.0f;
     if (center && k_mean) memcpy(k_mean + bg * d, mu, sizeof(float) * (size_t)d);
-    float A = 0.0f;
     for (int64_t n = 0; n < N; ++n) {
       for (int64_t c = 0; c < d; ++c) buf[n * d + c] = center ? src[n * d + c] - mu[c] : src[n * d + c];
       if (rotate) orc_fwht_row(buf + n * d, signs, d);
-      for (int64_t c = 0; c < d; ++c) { float a = fabsf(buf[n * d + c]); if (a > A) A = a; }
     }
-    float inv, desc;
-    scales_from_amax(A, rotate, d, &inv, &desc);
-    k_desc[bg] = desc;
-    for (int64_t e = 0; e < N * d; ++e) k8[bg * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+    float inv, desc, A;
+    for (int64_t t = 0; t < ngroup; ++t) {
+      int64_t e0 = t * span * d, e1 = ((t + 1) * span < N ? (t + 1) * span : N) * d;
+      A = 0.0f;
+      for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
+      scales_from_amax(A, rotate, d, &inv, &desc);
+      k_desc[bg * ngroup + t] = desc;
+      for (int64_t e = e0; e < e1; ++e) k8[bg * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+    }
 
     const float* vs = v + bg * N * d;
     A = 0.0f;
@@ -220,7 +229,7 @@ typedef struct {
   const float *qf, *kf, *vf;
   int64_t B, Hq, Hkv, N, d, nrows;
   float softmax_scale, p_scale;
-  int kv_order, block_n, causal, score_mode, p_cast;
+  int kv_order, block_n, causal, score_mode, p_cast, tiles;
   const int32_t* rows;
   float* out;
   uint8_t* p_out;
@@ -241,9 +250,11 @@ static void attn_row(void* p, int64_t item, double* scratch) {
   int fp8 = a->q8 != NULL;
   int64_t nvis = a->causal ? i + 1 : N;
 
-  /* Base-2 logit factor c = (desc_q * desc_k) * RN32(scale * log2 e). */
+  /* Base-2 logit factor c = (desc_q * desc_k) * RN32(scale * log2 e); with
+   * per-tile scales it is formed per block from the row's and block's tiles. */
   float ls2 = (float)((double)a->softmax_scale * LOG2E);
-  float c = fp8 ? (a->q_desc[bh] * a->k_desc[bg]) * ls2 : ls2;
+  int64_t ntile = (N + ORC_TILE_TOKENS - 1) / ORC_TILE_TOKENS;
+  float c = fp8 ? (a->tiles ? 0.0f : (a->q_desc[bh] * a->k_desc[bg]) * ls2) : ls2;
 
   double* s = scratch;
   float* acc = (float*)(scratch + N);
@@ -280,9 +291,19 @@ static void attn_row(void* p, int64_t item, double* scratch) {
     if (j0 >= j1) continue; /* no visible key: the block changes nothing */
     float bm = -INFINITY;
     for (int64_t j = j0; j < j1; ++j) if ((float)s[j] > bm) bm = (float)s[j];
-    float mnew = ms > bm ? ms : bm;
-    float mc = mnew * c;
-    float alpha = (ms == -INFINITY) ? 0.0f : orc_exp2_rn32(mc_prev - mc);
+    float mnew, mc, alpha;
+    if (a->tiles) {
+      /* running max in scaled units: m = max(m, RN32(bm * c_block)) */
+      c = (a->q_desc[bh * ntile + i / ORC_TILE_TOKENS] * a->k_desc[bg * ntile + j0 / ORC_TILE_TOKENS]) * ls2;
+      float bmc = bm * c;
+      mnew = -INFINITY; /* the raw max is not tracked here */
+      mc = mc_prev > bmc ? mc_prev : bmc;
+      alpha = (mc_prev == -INFINITY) ? 0.0f : orc_exp2_rn32(mc_prev - mc);
+    } else {
+      mnew = ms > bm ? ms : bm;
+      mc = mnew * c;
+      alpha = (ms == -INFINITY) ? 0.0f : orc_exp2_rn32(mc_prev - mc);
+    }
     l = l * alpha;
     for (int64_t cc = 0; cc < d; ++cc) acc[cc] = acc[cc] * alpha;
     for (int64_t j = j0; j < j1; ++j) {
@@ -306,7 +327,7 @@ static void attn_row(void* p, int64_t item, double* scratch) {
         for (int64_t cc = 0; cc < d; ++cc) acc[cc] = acc[cc] + pt * vr[cc];
       }
     }
-    ms = mnew;
+    if (!a->tiles) ms = mnew;
     mc_prev = mc;
   }
   float vd = fp8 ? a->v_desc[bg] : 1.0f;
@@ -341,6 +362,28 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
   a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
   a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.rows = rows; a.out = out;
+  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
+  return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
+}
+
+int orc_attention_fp8_tiles(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                            const float* q_desc, const float* k_desc, const float* v_desc,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                            float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
+                            const int32_t* rows, int64_t nrows,
+                            float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
+                            int score_mode, int nthreads) {
+  if (!q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc || !out || d > 128) return -1;
+  if (block_n <= 0 || ORC_TILE_TOKENS % block_n) return -1;
+  if (!rows) nrows = N;
+  int rc = check_loop(B, Hq, Hkv, N, d, p_scale, kv_order, block_n, rows, nrows);
+  if (rc) return rc;
+  loop_args a;
+  memset(&a, 0, sizeof a);
+  a.q8 = q8; a.k8 = k8; a.v8 = v8; a.q_desc = q_desc; a.k_desc = k_desc; a.v_desc = v_desc;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
+  a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
+  a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.tiles = 1; a.rows = rows; a.out = out;
   a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
   return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
 }

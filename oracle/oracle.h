@@ -23,6 +23,12 @@
 
 #define ORC_ROTATE 1u
 #define ORC_CENTER 2u
+/* One scale per 128-token tile for Q and K instead of per (batch, head): the
+ * earlier emulator's granularity, which the attention-numerics project page
+ * (second section) contrasts with FA3's full-sequence per-head scales.  V
+ * keeps one scale per (batch, KV head). */
+#define ORC_TILE 4u
+#define ORC_TILE_TOKENS 128
 
 /* E4M3FN codec: round to nearest, ties to even, saturating at +-448. */
 uint8_t orc_e4m3_encode(float x);
@@ -51,8 +57,9 @@ int orc_attention_f64(const double* q, const double* k, const double* v,
                       const int32_t* rows, int64_t nrows, double* out, int nthreads);
 
 /* Prologue emulation.  Inputs binary32 (BF16 inputs are widened exactly by
- * the caller).  Outputs: codes [B,H,N,d], descales [B*H], k_mean [B*Hkv*d]
- * (written when CENTER is set and k_mean is not NULL). */
+ * the caller).  Outputs: codes [B,H,N,d], descales [B*H] (with TILE: q_desc
+ * [B*Hq*T], k_desc [B*Hkv*T], T = ceil(N/128); v_desc stays [B*Hkv]), k_mean
+ * [B*Hkv*d] (written when CENTER is set and k_mean is not NULL). */
 int orc_prepare(const float* q, const float* k, const float* v,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                 uint32_t flags, const int8_t* signs,
@@ -67,6 +74,20 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                       const int32_t* rows, int64_t nrows,
                       float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
                       int score_mode, int nthreads);
+
+/* Main loop with per-tile Q/K descales (from a TILE prologue); block_n must
+ * divide 128.  The logit factor c depends on the row's query tile and the
+ * block's key tile, so the running max is kept in scaled units: per block
+ * m <- max(m, RN32(max_j s * c)), x = fma(s, c, -m), alpha = 2^(m_old - m).
+ * With one scale per head this is the per-head loop bit for bit (x -> RN32(x*c)
+ * is monotone for c > 0, so RN32(max_s * c) is the max of the blocks' values). */
+int orc_attention_fp8_tiles(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                            const float* q_desc, const float* k_desc, const float* v_desc,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                            float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
+                            const int32_t* rows, int64_t nrows,
+                            float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
+                            int score_mode, int nthreads);
 
 /* Main-loop emulation with binary32 Q/K/V (only P is cast). p_cast = 0
  * replaces the cast by the identity (structure checks). */
