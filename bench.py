@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-scales", action="store_true",
+                    help="one Q/K scale per 128-token tile (the variant) instead of per (batch, head)")
     ap.add_argument("--sample-tiles", type=int, default=3, help="query tiles per head in the CPU sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy (read + write of this many MiB), for scaling HBM counters")
@@ -129,7 +131,7 @@ def main():
         for cond in ("centered_rotated", "rotated"):
             fl = synth.CONDITIONS[cond]
             ta = time.perf_counter()
-            op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, **fl)
+            op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=args.tile_scales, **fl)
             emu = oracle.attention_fp8(op, p_scale=256.0, kv_order=1, block_n=128, causal=True, rows=rows)
             tb = time.perf_counter()
             if cond == "centered_rotated":
@@ -147,7 +149,7 @@ def main():
                           f"binary64 reference on the same rows {t_ideal:.1f}s")}
 
     ref = torch.from_numpy(ref_rows["f64"]).cuda() if ref_rows else torch.zeros((B, hq, rows.size, d), dtype=torch.float64, device="cuda")
-    prep = pipe.alloc_prepared()
+    prep = pipe.alloc_prepared(args.tile_scales)
     out = torch.empty((B, hq, N, d), dtype=torch.float32, device="cuda")
     rel = torch.empty(B * hq, dtype=torch.float64, device="cuda")
 
@@ -155,7 +157,7 @@ def main():
         fl = synth.CONDITIONS[cond]
         if ev is not None:
             ev[0].record()
-        pipe.prepare(q, k, v, signs=signs, prep=prep, **fl)
+        pipe.prepare(q, k, v, signs=signs, prep=prep, tiles=args.tile_scales, **fl)
         if ev is not None:
             ev[1].record()
         pipe.fwd(prep, p_scale=256.0, kv_order=1, block_n=128, causal=True, out=out)
@@ -210,11 +212,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "long-context causal FP8 attention forward, B=1, Hq=32, Hkv=8, d=128, N=%d, "
                                "BF16 sink-generator operands (Delta=8, 4 sinks), S=256, reverse KV order, block 128" % N,
-                   "condition": "centered_rotated", "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
+                   "condition": "centered_rotated",
+                   "qk_scales": "per 128-token tile" if args.tile_scales else "per (batch, head)",
+                   "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false>"),
-                     "kernel": "k_attn_fwd<128,128,2,causal,pow2>", "flop_per_launch": flop},
+                     "traffic": (None if args.tile_scales else
+                                 profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false, false>")),
+                     "kernel": "k_attn_fwd<128,128,2,causal,pow2%s>" % (",tiles" if args.tile_scales else ""),
+                     "flop_per_launch": flop},
         "cpu_baseline": cpu,
         "detail": results,
     }

@@ -48,6 +48,12 @@ typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3 } fp8a_d
  * second section; study page, same panel). */
 #define FP8A_ROTATE_QK 1u
 #define FP8A_CENTER_K 2u
+/* TILE_SCALES: one Q scale per (batch, query head, 128-token tile) and one K
+ * scale per (batch, KV head, tile) instead of per (batch, head) -- the earlier
+ * emulator's granularity, which the project page (second section) contrasts
+ * with FA3's full-sequence per-head scales; V keeps per-head scales.  Codes
+ * prepared this way go to fp8_attn_fwd_tile_scaled. */
+#define FP8A_TILE_SCALES 4u
 
 typedef struct {
   int32_t batch;     /* B >= 1 */
@@ -89,7 +95,10 @@ size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* shape, uint32_t flags)
  *   q8         device out, [B,hq,Np,d] E4M3FN codes.
  *   k8         device out, [B,hkv,Np,d] codes.
  *   v8t        device out, [B,hkv,d,Np] codes (V transposed: token axis contiguous).
- *   q_desc     device out, float[B*hq];  k_desc, v_desc: float[B*hkv].
+ *   q_desc     device out, float[B*hq];  k_desc, v_desc: float[B*hkv].  With
+ *              TILE_SCALES, q_desc float[B*hq*T] and k_desc float[B*hkv*T],
+ *              T = Np/128 (tile t covers tokens [128t, 128t+128); step 3's
+ *              max is taken per tile for Q and K).
  *   k_mean     device out, float[B*hkv*d]; written when CENTER (may be NULL).
  *   status_word device out, int32 (may be NULL): bit 0 is set when any input
  *              element was NaN or infinite; the codes are then unspecified.
@@ -150,6 +159,23 @@ int fp8_attn_fwd(const fp8a_shape* shape, fp8a_dtype qkv_dtype,
                  float softmax_scale, float p_scale, int32_t kv_order, int32_t block_n, int32_t causal,
                  float* out, float* lse, uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros,
                  int32_t k_sink, void* stream);
+
+/*
+ * fp8_attn_fwd_tile_scaled -- fp8_attn_fwd for codes from a TILE_SCALES
+ * prologue (E4M3 operands only).  q_desc is float[B*hq*T] and k_desc
+ * float[B*hkv*T] (T = Np/128); v_desc float[B*hkv].  The logit factor of query
+ * row i and block j is c = (q_desc[tile(i)] * k_desc[tile of block j]) *
+ * RN32(softmax_scale*log2 e), and the running max is kept in those scaled
+ * units: per block m <- max(m, RN32(max_j s * c)), x = fma(s, c, -m),
+ * alpha = 2^(m_old - m).  With equal scales in every tile this is
+ * fp8_attn_fwd bit for bit (x -> RN32(x*c) is monotone for c > 0).  Other
+ * arguments, outputs and errors as fp8_attn_fwd.
+ */
+int fp8_attn_fwd_tile_scaled(const fp8a_shape* shape, const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                             const float* q_desc, const float* k_desc, const float* v_desc,
+                             float softmax_scale, float p_scale, int32_t kv_order, int32_t block_n,
+                             int32_t causal, float* out, float* lse, uint8_t* p_dump, uint64_t* row_hash,
+                             uint32_t* row_zeros, int32_t k_sink, void* stream);
 
 /* Workspace needed by fp8_attn_head_error (bytes). */
 size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* shape, int64_t nrows);

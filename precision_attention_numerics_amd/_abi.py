@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8attn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8_attn.h")
 
 FP8A_F32, FP8A_BF16, FP8A_F64, FP8A_E4M3 = 0, 1, 2, 3
-FP8A_ROTATE_QK, FP8A_CENTER_K = 1, 2
+FP8A_ROTATE_QK, FP8A_CENTER_K, FP8A_TILE_SCALES = 1, 2, 4
 STATUS = {0: "FP8A_OK", -1: "FP8A_ERR_NULL", -2: "FP8A_ERR_SHAPE", -3: "FP8A_ERR_UNSUPPORTED",
           -4: "FP8A_ERR_PARAM", -5: "FP8A_ERR_WORKSPACE", -6: "FP8A_ERR_HIP"}
 
@@ -52,6 +52,9 @@ def _load():
     lib.fp8_attn_fwd.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, vp, vp, vp, vp, vp,
                                  i32, vp]
     lib.fp8_attn_fwd.restype = ctypes.c_int
+    lib.fp8_attn_fwd_tile_scaled.argtypes = [sp, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, vp, vp, vp, vp,
+                                             vp, i32, vp]
+    lib.fp8_attn_fwd_tile_scaled.restype = ctypes.c_int
     lib.fp8_attn_head_error_workspace_bytes.argtypes = [sp, i64]
     lib.fp8_attn_head_error_workspace_bytes.restype = sz
     lib.fp8_attn_head_error.argtypes = [sp, vp, vp, ctypes.c_int, vp, i64, vp, vp, sz, vp]
@@ -131,6 +134,17 @@ def fp8_attn_fwd(shape: Shape, qkv_dtype: int, q, k, v, q_desc, k_desc, v_desc, 
                            _ptr(row_zeros), int(k_sink), _stream(stream))
     if rc != 0:
         raise Fp8AttnError(rc, "fp8_attn_fwd")
+
+
+def fp8_attn_fwd_tile_scaled(shape: Shape, q8, k8, v8t, q_desc, k_desc, v_desc, softmax_scale: float,
+                             p_scale: float, kv_order: int, block_n: int, causal: int, out, lse=None, p_dump=None,
+                             row_hash=None, row_zeros=None, k_sink: int = 0, stream=None) -> None:
+    rc = _lib.fp8_attn_fwd_tile_scaled(ctypes.byref(shape), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_desc),
+                                       _ptr(k_desc), _ptr(v_desc), float(softmax_scale), float(p_scale),
+                                       int(kv_order), int(block_n), int(causal), _ptr(out), _ptr(lse),
+                                       _ptr(p_dump), _ptr(row_hash), _ptr(row_zeros), int(k_sink), _stream(stream))
+    if rc != 0:
+        raise Fp8AttnError(rc, "fp8_attn_fwd_tile_scaled")
 
 
 def fp8_attn_head_error(shape: Shape, out, ref, rows, nrows: int, rel_err, workspace, stream=None) -> None:

@@ -90,7 +90,8 @@ int32_t fp8_attn_padded_seqlen(int32_t seqlen) {
 size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* s, uint32_t flags) {
   if (check_shape(s) != FP8A_OK) return 0;
   const size_t B = s->batch, hq = s->hq, hkv = s->hkv, d = s->head_dim;
-  size_t bytes = align_up(B * (hq + 2 * hkv) * sizeof(uint32_t));
+  const size_t nt = (flags & FP8A_TILE_SCALES) ? static_cast<size_t>(fp8_attn_padded_seqlen(s->seqlen)) / 128 : 1;
+  size_t bytes = align_up(B * (hq * nt + hkv * nt + hkv) * sizeof(uint32_t));
   if (flags & FP8A_CENTER_K) {
     bytes += align_up(B * hkv * static_cast<size_t>(np2_chunks(s->seqlen)) * d * sizeof(double));
     bytes += align_up(B * hkv * d * sizeof(float));
@@ -105,7 +106,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   int rc = check_shape(s);
   if (rc) return rc;
   if (in_dtype != FP8A_F32 && in_dtype != FP8A_BF16) return FP8A_ERR_UNSUPPORTED;
-  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K)) return FP8A_ERR_PARAM;
+  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K | FP8A_TILE_SCALES)) return FP8A_ERR_PARAM;
   if (!q || !k || !v || !q8 || !k8 || !v8t || !q_desc || !k_desc || !v_desc) return FP8A_ERR_NULL;
   if ((flags & FP8A_ROTATE_QK) && !rot_signs) return FP8A_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
@@ -122,6 +123,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   a.bf16 = in_dtype == FP8A_BF16;
   a.rotate = (flags & FP8A_ROTATE_QK) != 0;
   a.center = (flags & FP8A_CENTER_K) != 0;
+  a.ntile = (flags & FP8A_TILE_SCALES) ? a.Np / 128 : 1;
   a.q = q; a.k = k; a.v = v;
   a.signs = rot_signs;
   a.cd = static_cast<float>(1.0 / sqrt(static_cast<double>(s->head_dim)));
@@ -130,7 +132,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   a.status = status_word;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.amax = reinterpret_cast<uint32_t*>(ws);
-  ws += align_up(static_cast<size_t>(a.B) * (a.hq + 2 * a.hkv) * sizeof(uint32_t));
+  ws += align_up(static_cast<size_t>(a.B) * (a.hq * a.ntile + a.hkv * a.ntile + a.hkv) * sizeof(uint32_t));
   a.np2 = np2_chunks(a.N);
   if (a.center) {
     a.mean_part = reinterpret_cast<double*>(ws);
@@ -140,13 +142,20 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   return hip_status(fp8a::launch_prepare(a, static_cast<hipStream_t>(stream)));
 }
 
-int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const void* k, const void* v,
-                 const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
-                 float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out, float* lse,
-                 uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forward entry points: tiles selects per-tile Q/K descales (E4M3 only).
+int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const void* k, const void* v,
+               const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
+               float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out, float* lse,
+               uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink, void* stream,
+               bool tiles) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32) return FP8A_ERR_UNSUPPORTED;
+  if (tiles && qkv_dtype != FP8A_E4M3) return FP8A_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out) return FP8A_ERR_NULL;
   // the E4M3 kernel addresses one head's K8 / V8t through a buffer resource
   // with a 31-bit byte range
@@ -184,6 +193,7 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
   p.out = out; p.lse = lse; p.p_dump = p_dump; p.row_hash = row_hash; p.row_zeros = row_zeros;
   p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.Np = fp8_attn_padded_seqlen(s->seqlen);
   p.n_qtiles = p.Np / 128; p.kv_order = kv_order; p.k_sink = k_sink;
+  p.tiles = tiles ? 1 : 0;
   p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
   {
     float x0, x1;
@@ -195,6 +205,27 @@ int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const
   }
   const bool dump = p_dump != nullptr || row_hash != nullptr || row_zeros != nullptr;
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_attn_fwd(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const void* k, const void* v,
+                 const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
+                 float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out, float* lse,
+                 uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink, void* stream) {
+  return fwd_common(s, qkv_dtype, q, k, v, q_desc, k_desc, v_desc, softmax_scale, p_scale, kv_order, block_n,
+                    causal, out, lse, p_dump, row_hash, row_zeros, k_sink, stream, false);
+}
+
+int fp8_attn_fwd_tile_scaled(const fp8a_shape* s, const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                             const float* q_desc, const float* k_desc, const float* v_desc, float softmax_scale,
+                             float p_scale, int32_t kv_order, int32_t block_n, int32_t causal, float* out,
+                             float* lse, uint8_t* p_dump, uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink,
+                             void* stream) {
+  return fwd_common(s, FP8A_E4M3, q8, k8, v8t, q_desc, k_desc, v_desc, softmax_scale, p_scale, kv_order, block_n,
+                    causal, out, lse, p_dump, row_hash, row_zeros, k_sink, stream, true);
 }
 
 size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* s, int64_t nrows) {

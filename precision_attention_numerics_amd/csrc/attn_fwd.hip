@@ -242,7 +242,7 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
 // Online-softmax update of one 16-row query tile for one block and the P
 // cast.  The lane holds query i and keys jb + 4t + r (t < T, r < 4); s holds
 // the scores on entry and x = s*c - RN32(m*c) on exit.
-template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
+template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP, bool TILES>
 __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], const float c, float& ms, float& mcp,
                                                                   float& lsum, v4f (&oacc)[D / 16], const int i,
                                                                   const int jb, const int N, const FwdParams& p,
@@ -264,8 +264,19 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
     for (int t = 1; t < T; ++t) m4[r] = fmax_nan(m4[r], s[t][r]);
   }
   const float bm = column_max(fmax_nan(fmax_nan(m4[0], m4[1]), fmax_nan(m4[2], m4[3])));
+  // ms: running max of the raw scores; mcp: running max in scaled units
+  // RN32(m * c), 0 while no key has been visible.  With per-tile scales c
+  // changes from block to block, so mcp is carried as the max of RN32(bm * c)
+  // over the blocks; with one c per row both forms are the same value
+  // (rounding is monotone).
   const float mnew = fmax_nan(ms, bm);
-  const float mc = (mnew == -INFINITY) ? 0.0f : mnew * c;
+  float mc;
+  if constexpr (TILES) {
+    const float bmc = (bm == -INFINITY) ? -INFINITY : bm * c;
+    mc = (mnew == -INFINITY) ? 0.0f : ((ms == -INFINITY) ? bmc : fmax_nan(mcp, bmc));
+  } else {
+    mc = (mnew == -INFINITY) ? 0.0f : mnew * c;
+  }
   const float alpha = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mcp - mc);
   lsum = lsum * alpha;
   // Unconditional: alpha is exactly 1 when the max did not move, and a
@@ -312,7 +323,7 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
   return out;
 }
 
-template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP>
+template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP, bool TILES>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   constexpr int QROWS = kWaves * QT * 16;
   static_assert(QROWS == 128, "query tile must match the 128-token padding");
@@ -344,7 +355,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   const int bg = b * p.hkv + g;
   const int N = p.N, Np = p.Np;
   const int q0 = qtile * QROWS;
-  const float c = (p.q_desc[bh] * p.k_desc[bg]) * p.ls2;
+  // base-2 logit factor (q_desc * k_desc) * RN32(scale * log2 e): per head, or
+  // per block from the query tile's and the block's key tile's descales
+  const float qd = TILES ? p.q_desc[static_cast<int64_t>(bh) * nqt + qtile] : p.q_desc[bh];
+  const float c_head = TILES ? 0.0f : (qd * p.k_desc[bg]) * p.ls2;
   const float vdesc = p.v_desc[bg];
 
   // wv is wave-uniform; readfirstlane lets the compiler keep it (and every
@@ -416,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
                         vlds + (KBYTES - cur));
     const uint8_t* kt = klds + cur;
     const uint8_t* vt = vlds + cur;
+    const float c = TILES ? (qd * p.k_desc[static_cast<int64_t>(bg) * nqt + (j0 >> 7)]) * p.ls2 : c_head;
 
     // ---- S^T = K Q^T for both 16-row query tiles from one LDS read of each K
     // tile, then per query tile the online softmax and the P cast; the lane
@@ -442,10 +457,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       uint8_t* drow = nullptr;
       if constexpr (DUMP) drow = p.p_dump ? p.p_dump + (static_cast<int64_t>(bh) * N + i) * N : nullptr;
       if (DUMP || need_mask)
-        pop[qt] = softmax_tile<D, T, true, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
+        pop[qt] = softmax_tile<D, T, true, CAUSAL, POW2, DUMP, TILES>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
                                                               j0 + KPL * lg, N, p, zeros[qt], hash[qt], drow);
       else
-        pop[qt] = softmax_tile<D, T, false, CAUSAL, POW2, DUMP>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
+        pop[qt] = softmax_tile<D, T, false, CAUSAL, POW2, DUMP, TILES>(sacc, c, ms[qt], mcp[qt], lsum[qt], oacc[qt], i,
                                                                j0 + KPL * lg, N, p, zeros[qt], hash[qt], drow);
     }
 
@@ -567,7 +582,8 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
 template <int D, int BC, bool CAUSAL, bool POW2, bool DUMP>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.B * p.hq * p.n_qtiles));
-  k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP><<<grid, dim3(kThreads), 0, st>>>(p);
+  if (p.tiles) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, true><<<grid, dim3(kThreads), 0, st>>>(p);
+  else k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false><<<grid, dim3(kThreads), 0, st>>>(p);
   return hipGetLastError();
 }
 

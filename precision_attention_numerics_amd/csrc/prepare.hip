@@ -206,19 +206,22 @@ constexpr int kPrepThreads = 256;
 constexpr int kRowsPerBlock = 256;
 constexpr int kRowsInFlight = 4;
 
-// Per-head max |x| of the transformed rows.  grid = (ceil(N / 256), B*H).
+// Max |x| of the transformed rows per head (ntile == 1) or per 128-token tile
+// of a head (amax[bh * ntile + tile]).  grid = (ceil(N / 256), B*H): a block's
+// rows are tiles 2*bx and 2*bx + 1.
 template <typename IT, int D, bool ROT, bool CENTER>
 __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
                                                        int32_t H, int32_t N, const float* __restrict__ mu_all,
                                                        int32_t hq_per_mu, const int8_t* __restrict__ signs,
-                                                       uint32_t* __restrict__ amax, int32_t* __restrict__ status) {
+                                                       int32_t ntile, uint32_t* __restrict__ amax,
+                                                       int32_t* __restrict__ status) {
   constexpr int L = D / 8;                 // lanes per row
   constexpr int RPI = kPrepThreads / L;    // rows per iteration
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
   const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
   const IT* base = x + b * sb + h * sh + 8 * li;
-  float m = 0.0f;
+  float m = 0.0f, m_hi = 0.0f;   // rows [0, 128) and [128, 256) of the block
   bool bad = false;
   const int n_begin = blockIdx.x * kRowsPerBlock;
   // kRowsInFlight rows per lane group per step, loaded before any is
@@ -244,25 +247,41 @@ __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x,
       for (int e = 0; e < 8; ++e) bad |= live && !__builtin_isfinite(v[u][e]);
       transform_row<D, ROT, CENTER>(v[u], li, mu, signs);
       if (live) {
+        float rm = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[u][e]));
+        for (int e = 0; e < 8; ++e) rm = __builtin_fmaxf(rm, __builtin_fabsf(v[u][e]));
+        if (r0 + u * RPI < kRowsPerBlock / 2) m = __builtin_fmaxf(m, rm);
+        else m_hi = __builtin_fmaxf(m_hi, rm);
       }
     }
   }
+  if (ntile == 1) m = __builtin_fmaxf(m, m_hi);
 #pragma unroll
-  for (int s = 1; s < kWave; s <<= 1) m = __builtin_fmaxf(m, wave_xor(m, s));
-  __shared__ float red[kPrepThreads / kWave];
+  for (int s = 1; s < kWave; s <<= 1) {
+    m = __builtin_fmaxf(m, wave_xor(m, s));
+    m_hi = __builtin_fmaxf(m_hi, wave_xor(m_hi, s));
+  }
+  __shared__ float red[2][kPrepThreads / kWave];
   __shared__ int redbad;
   if (threadIdx.x == 0) redbad = 0;
   __syncthreads();
   if (bad) atomicOr(&redbad, 1);
-  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = m;
+  if (threadIdx.x % kWave == 0) {
+    red[0][threadIdx.x / kWave] = m;
+    red[1][threadIdx.x / kWave] = m_hi;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float mm = red[0];
-    for (int w = 1; w < kPrepThreads / kWave; ++w) mm = __builtin_fmaxf(mm, red[w]);
-    atomicMax(amax + bh, __float_as_uint(mm));
-    if (redbad && status) atomicOr(status, 1);
+  if (threadIdx.x < 2) {
+    const int half = threadIdx.x;
+    float mm = red[half][0];
+    for (int w = 1; w < kPrepThreads / kWave; ++w) mm = __builtin_fmaxf(mm, red[half][w]);
+    if (ntile == 1) {
+      if (half == 0) atomicMax(amax + bh, __float_as_uint(mm));
+    } else if (n_begin + half * (kRowsPerBlock / 2) < N) {
+      // each tile is written by exactly one block
+      atomicMax(amax + static_cast<int64_t>(bh) * ntile + 2 * blockIdx.x + half, __float_as_uint(mm));
+    }
+    if (half == 0 && redbad && status) atomicOr(status, 1);
   }
 }
 
@@ -275,23 +294,36 @@ __device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, f
 }
 
 // Quantise Q or K rows into [B,H,Np,D] codes; rows in [N, Np) are written as 0.
+// Scales per head (ntile == 1) or per 128-token tile (desc_out[bh * ntile + t]).
 template <typename IT, int D, bool ROT, bool CENTER>
 __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
                                                              int32_t H, int32_t N, int32_t Np, const float* __restrict__ mu_all,
                                                              int32_t hq_per_mu, const int8_t* __restrict__ signs,
-                                                             const uint32_t* __restrict__ amax, float cd,
+                                                             int32_t ntile, const uint32_t* __restrict__ amax, float cd,
                                                              float* __restrict__ desc_out, uint8_t* __restrict__ codes) {
   constexpr int L = D / 8;
   constexpr int RPI = kPrepThreads / L;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
   const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
-  float inv, desc;
-  scales_from_amax(amax[bh], ROT, cd, inv, desc);
-  if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+  const int n_begin = blockIdx.x * kRowsPerBlock;
+  // scales of the block's rows [0, 128) and [128, 256)
+  float inv, desc, inv_hi, desc_hi;
+  if (ntile == 1) {
+    scales_from_amax(amax[bh], ROT, cd, inv, desc);
+    inv_hi = inv;
+    desc_hi = desc;
+    if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+  } else {
+    const int64_t t0 = static_cast<int64_t>(bh) * ntile + 2 * blockIdx.x;
+    const bool has_hi = n_begin + kRowsPerBlock / 2 < Np;   // the block's second tile exists
+    scales_from_amax(amax[t0], ROT, cd, inv, desc);
+    scales_from_amax(has_hi ? amax[t0 + 1] : 0u, ROT, cd, inv_hi, desc_hi);
+    if (threadIdx.x == 0) desc_out[t0] = desc;
+    if (threadIdx.x == 1 && has_hi) desc_out[t0 + 1] = desc_hi;
+  }
   const IT* base = x + b * sb + h * sh + 8 * li;
   uint8_t* out = codes + static_cast<int64_t>(bh) * Np * D + 8 * li;
-  const int n_begin = blockIdx.x * kRowsPerBlock;
   // kRowsInFlight rows per lane group per step, loaded before any is
   // transformed (the L lanes of a row share r, so its lane exchanges always run
   // on all of them).
@@ -313,11 +345,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
       transform_row<D, ROT, CENTER>(v[u], li, mu, signs);
       uint2 w = make_uint2(0u, 0u);
       if (n < N) {
+        const float s = (r0 + u * RPI < kRowsPerBlock / 2) ? inv : inv_hi;
         uint32_t lo = 0, hi = 0;
-        lo = e4m3_pack2<false>(v[u][0] * inv, v[u][1] * inv, lo);
-        lo = e4m3_pack2<true>(v[u][2] * inv, v[u][3] * inv, lo);
-        hi = e4m3_pack2<false>(v[u][4] * inv, v[u][5] * inv, hi);
-        hi = e4m3_pack2<true>(v[u][6] * inv, v[u][7] * inv, hi);
+        lo = e4m3_pack2<false>(v[u][0] * s, v[u][1] * s, lo);
+        lo = e4m3_pack2<true>(v[u][2] * s, v[u][3] * s, lo);
+        hi = e4m3_pack2<false>(v[u][4] * s, v[u][5] * s, hi);
+        hi = e4m3_pack2<true>(v[u][6] * s, v[u][7] * s, hi);
         w = make_uint2(lo, hi);
       }
       // rows in [N, Np) are written as zero codes
@@ -382,12 +415,13 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   const IT* q = static_cast<const IT*>(a.q);
   const IT* k = static_cast<const IT*>(a.k);
   const IT* v = static_cast<const IT*>(a.v);
-  const int64_t n_amax = static_cast<int64_t>(B) * (hq + 2 * hkv);
+  const int32_t nt = a.ntile;
+  const int64_t n_amax = static_cast<int64_t>(B) * (hq * nt + hkv * nt + hkv);
   k_fill_u32<<<dim3(static_cast<unsigned>((n_amax + 255) / 256)), blk, 0, st>>>(a.amax, 0u, n_amax);
   if (a.status) k_fill_u32<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<uint32_t*>(a.status), 0u, 1);
   uint32_t* amax_q = a.amax;
-  uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq;
-  uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv;
+  uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq * nt;
+  uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv * nt;
   if (a.center) {
     constexpr int32_t kChunksPerBlock = 256 / (D / 8);
     k_kmean_partial<IT, D><<<dim3((a.np2 + kChunksPerBlock - 1) / kChunksPerBlock, B * hkv), dim3(256), 0, st>>>(
@@ -400,31 +434,31 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   const dim3 gk_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
   const float* mu = a.k_mean;
   if (a.rotate) {
-    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, amax_q, a.status);
+    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, nt, amax_q, a.status);
     if (a.center)
-      k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, a.signs, amax_k, a.status);
+      k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, a.signs, nt, amax_k, a.status);
     else
-      k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, a.signs, amax_k, a.status);
+      k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, a.signs, nt, amax_k, a.status);
   } else {
-    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, amax_q, a.status);
+    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, nt, amax_q, a.status);
     if (a.center)
-      k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, amax_k, a.status);
+      k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, nt, amax_k, a.status);
     else
-      k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, amax_k, a.status);
+      k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, nt, amax_k, a.status);
   }
-  k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, amax_v, a.status);
+  k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, 1, amax_v, a.status);
   if (a.rotate) {
-    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, amax_q, a.cd, a.q_desc, a.q8);
+    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, a.q_desc, a.q8);
     if (a.center)
-      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, nt, amax_k, a.cd, a.k_desc, a.k8);
     else
-      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, nt, amax_k, a.cd, a.k_desc, a.k8);
   } else {
-    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, amax_q, a.cd, a.q_desc, a.q8);
+    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, a.q_desc, a.q8);
     if (a.center)
-      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, a.k_desc, a.k8);
     else
-      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, a.k_desc, a.k8);
   }
   k_quant_vt<IT, D><<<dim3(Np / 128, B * hkv), blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, Np, amax_v, a.v_desc, a.v8t);
   (void)grp;

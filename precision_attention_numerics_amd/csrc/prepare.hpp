@@ -8,6 +8,7 @@ namespace fp8a {
 struct PrepareArgs {
   int32_t B, hq, hkv, N, Np, D;
   bool bf16, rotate, center;
+  int32_t ntile;                 // Q/K scale groups per head: Np/128 with per-tile scales, else 1
   const void *q, *k, *v;
   int64_t qs[3], ks[3], vs[3];   // element strides of (batch, head, token)
   const int8_t* signs;
@@ -15,7 +16,7 @@ struct PrepareArgs {
   uint8_t *q8, *k8, *v8t;
   float *q_desc, *k_desc, *v_desc, *k_mean;
   int32_t* status;               // may be null
-  uint32_t* amax;                // workspace: B*(hq + 2*hkv)
+  uint32_t* amax;                // workspace: B*(hq*ntile + hkv*ntile + hkv)
   double* mean_part;             // workspace: B*hkv*np2*D (CENTER only)
   int32_t np2;                   // chunk count rounded up to a power of two
 };

@@ -15,11 +15,12 @@ class Prepared:
     q8: torch.Tensor       # [B,hq,Np,d] uint8
     k8: torch.Tensor       # [B,hkv,Np,d] uint8
     v8t: torch.Tensor      # [B,hkv,d,Np] uint8
-    q_desc: torch.Tensor   # [B*hq] float32
-    k_desc: torch.Tensor   # [B*hkv]
+    q_desc: torch.Tensor   # [B*hq] float32, or [B*hq*T] with per-tile scales (T = Np/128)
+    k_desc: torch.Tensor   # [B*hkv], or [B*hkv*T]
     v_desc: torch.Tensor   # [B*hkv]
     k_mean: torch.Tensor   # [B*hkv*d] (valid after a centred prepare)
     status: torch.Tensor   # [1] int32
+    tiles: bool = False    # Q/K descales per 128-token tile
 
 
 class AttnPipeline:
@@ -37,19 +38,25 @@ class AttnPipeline:
             self._ws[key] = t
         return t
 
-    def alloc_prepared(self) -> Prepared:
+    def alloc_prepared(self, tiles: bool = False) -> Prepared:
         B, hq, hkv, Np, d, dev = self.B, self.hq, self.hkv, self.Np, self.d, self.device
+        T = Np // 128 if tiles else 1
         u8 = dict(dtype=torch.uint8, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         return Prepared(torch.empty((B, hq, Np, d), **u8), torch.empty((B, hkv, Np, d), **u8),
-                        torch.empty((B, hkv, d, Np), **u8), torch.empty(B * hq, **f32),
-                        torch.empty(B * hkv, **f32), torch.empty(B * hkv, **f32),
-                        torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev))
+                        torch.empty((B, hkv, d, Np), **u8), torch.empty(B * hq * T, **f32),
+                        torch.empty(B * hkv * T, **f32), torch.empty(B * hkv, **f32),
+                        torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev), tiles)
 
     def prepare(self, q, k, v, rotate: bool, center: bool, signs=None, prep: Prepared | None = None,
-                stream=None) -> Prepared:
-        prep = prep or self.alloc_prepared()
-        flags = (_abi.FP8A_ROTATE_QK if rotate else 0) | (_abi.FP8A_CENTER_K if center else 0)
+                stream=None, tiles: bool = False) -> Prepared:
+        """tiles: one Q/K scale per 128-token tile (FP8A_TILE_SCALES); the
+        forward then uses fp8_attn_fwd_tile_scaled."""
+        prep = prep or self.alloc_prepared(tiles)
+        if prep.tiles != tiles:
+            raise ValueError("prepared buffers were allocated for the other scale granularity")
+        flags = ((_abi.FP8A_ROTATE_QK if rotate else 0) | (_abi.FP8A_CENTER_K if center else 0)
+                 | (_abi.FP8A_TILE_SCALES if tiles else 0))
         shape = _abi.make_shape(self.B, self.hq, self.hkv, self.N, self.d, q, k, v)
         ws = self._workspace("prep", _abi.prepare_workspace_bytes(shape, flags))
         _abi.fp8_attn_prepare(shape, q, k, v, flags, signs if rotate else None, prep.q8, prep.k8, prep.v8t,
@@ -64,9 +71,15 @@ class AttnPipeline:
             softmax_scale = 1.0 / math.sqrt(self.d)
         if out is None:
             out = torch.empty((self.B, self.hq, self.N, self.d), dtype=torch.float32, device=self.device)
-        _abi.fp8_attn_fwd(self.shape, _abi.FP8A_E4M3, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
-                          prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse=lse,
-                          p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros, k_sink=k_sink, stream=stream)
+        if prep.tiles:
+            _abi.fp8_attn_fwd_tile_scaled(self.shape, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
+                                          prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal),
+                                          out, lse=lse, p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros,
+                                          k_sink=k_sink, stream=stream)
+        else:
+            _abi.fp8_attn_fwd(self.shape, _abi.FP8A_E4M3, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
+                              prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse=lse,
+                              p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros, k_sink=k_sink, stream=stream)
         return out
 
     def fwd_f32(self, q, k, v, p_scale: float = 256.0, kv_order: int = 0, block_n: int = 128,

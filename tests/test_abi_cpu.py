@@ -61,6 +61,8 @@ def test_workspace_sizes(abi):
     assert base >= (32 + 16) * 4 and cen > base
     assert cen - base >= 8 * 512 * 128 * 8          # 512 chunk partials per KV head and channel
     assert abi.head_error_workspace_bytes(s, 32768) >= 32 * 2 * 8
+    tiles = abi.prepare_workspace_bytes(s, abi.FP8A_TILE_SCALES)
+    assert tiles - base >= (32 + 8) * (256 - 1) * 4      # one max slot per 128-token tile of Q and K heads
     bad = abi.make_shape(1, 3, 2, 16, 128)           # hq % hkv != 0
     assert abi.prepare_workspace_bytes(bad, 0) == 0
 
@@ -98,6 +100,7 @@ def test_prepare_rejects(abi):
     assert _prep(abi, abi.make_shape(1, 2, 1, 0, 64)) == -2           # seqlen
     assert _prep(abi, ok, dtype=2) == -3                               # f64 input
     assert _prep(abi, ok, flags=8) == -4                               # unknown flag
+    assert _prep(abi, ok, flags=abi.FP8A_TILE_SCALES, ws_bytes=1) == -5   # tile maxima need workspace too
     assert _prep(abi, ok, q=None) == -1
     assert _prep(abi, ok, flags=abi.FP8A_ROTATE_QK, signs=None) == -1
     assert _prep(abi, ok, ws=None) == -5
@@ -127,6 +130,20 @@ def test_fwd_rejects(abi):
     assert _fwd(abi, ok, desc=None) == -1
     assert _fwd(abi, ok, out=None) == -1
     assert _fwd(abi, abi.make_shape(1, 2, 1, 64, 32)) == -2
+
+
+def test_fwd_tile_scaled_rejects(abi):
+    _no_gpu()
+    ok = abi.make_shape(1, 2, 1, 64, 64)
+
+    def call(shape=ok, desc=FAKE, out=FAKE, S=256.0, bn=128):
+        return abi._lib.fp8_attn_fwd_tile_scaled(ctypes.byref(shape), FAKE, FAKE, FAKE, desc, desc, desc, 0.125, S,
+                                                 1, bn, 1, out, None, None, None, None, 0, None)
+    assert call(desc=None) == -1
+    assert call(out=None) == -1
+    assert call(S=100.0) == -3
+    assert call(bn=32) == -4
+    assert call(shape=abi.make_shape(1, 2, 1, 64, 32)) == -2
 
 
 def test_head_error_rejects(abi):
