@@ -44,6 +44,7 @@ _lib = None
 ROTATE = 1
 CENTER = 2
 TILE = 4
+PREFIX = 8
 TILE_TOKENS = 128
 SCORE_MODES = {"mfma": 0, "exact": 1}
 
@@ -201,11 +202,14 @@ class Prepared:
     tiles: bool = False     # q_desc [B,Hq,T] / k_desc [B,Hkv,T] per 128-token tile
 
 
-def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, tiles: bool = False) -> Prepared:
+def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, tiles: bool = False,
+            prefix: bool = False) -> Prepared:
     """Quantisation prologue on binary32 operands (BF16 widened exactly).
     tiles: one Q/K scale per 128-token tile instead of per (batch, head) (the
     earlier emulator's granularity, attention-numerics project page, second
-    section); V keeps per-head scales."""
+    section); V keeps per-head scales.  prefix (with tiles, without center):
+    tile t's Q/K scale from the largest maximum among tiles 0..t, so no scale
+    depends on tokens past its tile."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     v = np.ascontiguousarray(v, dtype=np.float32)
@@ -220,7 +224,8 @@ def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, til
     kd = np.empty(B * Hkv * T, np.float32)
     vd = np.empty(B * Hkv, np.float32)
     km = np.empty(B * Hkv * d, np.float32) if center else None
-    flags = (ROTATE if rotate else 0) | (CENTER if center else 0) | (TILE if tiles else 0)
+    flags = ((ROTATE if rotate else 0) | (CENTER if center else 0) | (TILE if tiles else 0)
+             | (PREFIX if prefix else 0))
     rc = _load().orc_prepare(_p(q, _c_f32p), _p(k, _c_f32p), _p(v, _c_f32p), B, Hq, Hkv, N, d, flags,
                              _p(s, _c_i8p), _p(q8, _c_u8p), _p(k8, _c_u8p), _p(v8, _c_u8p),
                              _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p), _p(km, _c_f32p))

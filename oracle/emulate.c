@@ -71,7 +71,8 @@ int orc_prepare(const float* q, const float* k, const float* v,
   if (!q || !k || !v || !q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc) return -1;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv || (d & (d - 1))) return -1;
   int rotate = (flags & ORC_ROTATE) != 0, center = (flags & ORC_CENTER) != 0;
-  int tiled = (flags & ORC_TILE) != 0;
+  int tiled = (flags & ORC_TILE) != 0, prefix = (flags & ORC_PREFIX) != 0;
+  if (prefix && (!tiled || center)) return -1;
   /* scale groups: the whole sequence, or 128-token tiles */
   int64_t span = tiled ? ORC_TILE_TOKENS : N, ngroup = (N + span - 1) / span;
   if (rotate && !signs) return -1;
@@ -90,10 +91,12 @@ int orc_prepare(const float* q, const float* k, const float* v,
       memcpy(buf + n * d, src + n * d, sizeof(float) * (size_t)d);
       if (rotate) orc_fwht_row(buf + n * d, signs, d);
     }
+    float Apre = 0.0f;
     for (int64_t t = 0; t < ngroup; ++t) {
       int64_t e0 = t * span * d, e1 = ((t + 1) * span < N ? (t + 1) * span : N) * d;
       float A = 0.0f;
       for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
+      if (prefix) { if (A > Apre) Apre = A; A = Apre; }
       float inv, desc;
       scales_from_amax(A, rotate, d, &inv, &desc);
       q_desc[bh * ngroup + t] = desc;
@@ -109,11 +112,12 @@ int orc_prepare(const float* q, const float* k, const float* v,
       for (int64_t c = 0; c < d; ++c) buf[n * d + c] = center ? src[n * d + c] - mu[c] : src[n * d + c];
       if (rotate) orc_fwht_row(buf + n * d, signs, d);
     }
-    float inv, desc, A;
+    float inv, desc, A, Apre = 0.0f;
     for (int64_t t = 0; t < ngroup; ++t) {
       int64_t e0 = t * span * d, e1 = ((t + 1) * span < N ? (t + 1) * span : N) * d;
       A = 0.0f;
       for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
+      if (prefix) { if (A > Apre) Apre = A; A = Apre; }
       scales_from_amax(A, rotate, d, &inv, &desc);
       k_desc[bg * ngroup + t] = desc;
       for (int64_t e = e0; e < e1; ++e) k8[bg * N * d + e] = orc_e4m3_encode(buf[e] * inv);

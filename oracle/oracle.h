@@ -29,6 +29,11 @@
  * keeps one scale per (batch, KV head). */
 #define ORC_TILE 4u
 #define ORC_TILE_TOKENS 128
+/* With TILE: tile t's Q and K scales come from the largest tile maximum among
+ * tiles 0..t (prefix scales: no scale depends on tokens past its tile's end,
+ * the caveat the project page raises about full-sequence scales).  Not
+ * combined with CENTER (one K code set cannot carry a per-query prefix mean). */
+#define ORC_PREFIX 8u
 
 /* E4M3FN codec: round to nearest, ties to even, saturating at +-448. */
 uint8_t orc_e4m3_encode(float x);

@@ -112,3 +112,48 @@ def test_loop_matches_softmax_of_dequantised_operands(order):
     out = oracle.attention_fp8(p, kv_order=order).out[0].astype(np.float64)
     rel = np.sqrt(((out - ref) ** 2).sum((-2, -1)) / (ref ** 2).sum((-2, -1)))
     assert rel.max() < 2e-2, rel
+
+
+def test_prefix_scales_are_running_maxima_of_tile_maxima():
+    """Prefix scales: tile t uses the largest tile maximum among tiles 0..t;
+    where tile maxima only grow they equal the plain tile scales, and codes of
+    a tile whose scale comes from an earlier tile are that tile's values at the
+    earlier scale."""
+    N = 640
+    q, k, v = operands(6, N, tile_gain=(2.0, 0.5, 1.0, 4.0, 0.25))
+    a = oracle.prepare(q, k, v, rotate=True, signs=signs(64), tiles=True)
+    b = oracle.prepare(q, k, v, rotate=True, signs=signs(64), tiles=True, prefix=True)
+    for x, y in ((a.q_desc, b.q_desc), (a.k_desc, b.k_desc)):
+        assert np.array_equal(np.maximum.accumulate(x, axis=-1), y)
+        assert np.all(np.diff(y, axis=-1) >= 0)
+    # the first tile never changes; where the running max moves, codes match the tile-scaled ones
+    same = (a.q_desc == b.q_desc)[0, 0]
+    for t in np.nonzero(same)[0]:
+        assert np.array_equal(a.q8[0, 0, 128 * t:128 * (t + 1)], b.q8[0, 0, 128 * t:128 * (t + 1)])
+    assert same[0] and not same.all()
+
+
+def test_prefix_scales_reject_centering():
+    q, k, v = operands(7, 256)
+    with pytest.raises(RuntimeError):
+        oracle.prepare(q, k, v, center=True, tiles=True, prefix=True)
+    with pytest.raises(RuntimeError):
+        oracle.prepare(q, k, v, prefix=True)
+
+
+def test_prefix_scales_ignore_future_tiles():
+    """Changing tokens of tile 2 and later leaves the codes and scales of tiles
+    0 and 1 untouched (the causality the prefix reading is for)."""
+    N = 512
+    q, k, v = operands(8, N)
+    a = oracle.prepare(q, k, v, tiles=True, prefix=True)
+    q2, k2 = q.copy(), k.copy()
+    q2[:, :, 256:] *= np.float32(8.0)
+    k2[:, :, 300:] += np.float32(5.0)
+    b = oracle.prepare(q2, k2, v, tiles=True, prefix=True)
+    assert np.array_equal(a.q8[:, :, :256], b.q8[:, :, :256]) and np.array_equal(a.k8[:, :, :256], b.k8[:, :, :256])
+    assert np.array_equal(a.q_desc[..., :2], b.q_desc[..., :2]) and np.array_equal(a.k_desc[..., :2], b.k_desc[..., :2])
+    assert not np.array_equal(a.q_desc[..., 2:], b.q_desc[..., 2:])
+    # with full-sequence scales the same change reaches the early tiles' codes
+    c, e = oracle.prepare(q, k, v), oracle.prepare(q2, k2, v)
+    assert not np.array_equal(c.q8[:, :, :256], e.q8[:, :, :256])
