@@ -54,6 +54,13 @@ typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3 } fp8a_d
  * with FA3's full-sequence per-head scales; V keeps per-head scales.  Codes
  * prepared this way go to fp8_attn_fwd_tile_scaled. */
 #define FP8A_TILE_SCALES 4u
+/* PREFIX_SCALES (with TILE_SCALES, without CENTER_K): tile t's Q and K scales
+ * come from the largest tile maximum among tiles 0..t, so no scale depends on
+ * tokens past its own tile (the project page notes that full-sequence means
+ * and scales see future tokens).  Causal at the 128-token tile granularity.
+ * Errors: FP8A_ERR_PARAM without TILE_SCALES, FP8A_ERR_UNSUPPORTED with
+ * CENTER_K (one set of K codes cannot carry a per-query prefix mean). */
+#define FP8A_PREFIX_SCALES 8u
 
 typedef struct {
   int32_t batch;     /* B >= 1 */

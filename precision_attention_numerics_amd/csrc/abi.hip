@@ -106,7 +106,9 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   int rc = check_shape(s);
   if (rc) return rc;
   if (in_dtype != FP8A_F32 && in_dtype != FP8A_BF16) return FP8A_ERR_UNSUPPORTED;
-  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K | FP8A_TILE_SCALES)) return FP8A_ERR_PARAM;
+  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K | FP8A_TILE_SCALES | FP8A_PREFIX_SCALES)) return FP8A_ERR_PARAM;
+  if ((flags & FP8A_PREFIX_SCALES) && !(flags & FP8A_TILE_SCALES)) return FP8A_ERR_PARAM;
+  if ((flags & FP8A_PREFIX_SCALES) && (flags & FP8A_CENTER_K)) return FP8A_ERR_UNSUPPORTED;
   if (!q || !k || !v || !q8 || !k8 || !v8t || !q_desc || !k_desc || !v_desc) return FP8A_ERR_NULL;
   if ((flags & FP8A_ROTATE_QK) && !rot_signs) return FP8A_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
@@ -124,6 +126,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   a.rotate = (flags & FP8A_ROTATE_QK) != 0;
   a.center = (flags & FP8A_CENTER_K) != 0;
   a.ntile = (flags & FP8A_TILE_SCALES) ? a.Np / 128 : 1;
+  a.prefix = (flags & FP8A_PREFIX_SCALES) != 0;
   a.q = q; a.k = k; a.v = v;
   a.signs = rot_signs;
   a.cd = static_cast<float>(1.0 / sqrt(static_cast<double>(s->head_dim)));

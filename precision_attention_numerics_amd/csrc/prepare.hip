@@ -285,6 +285,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x,
   }
 }
 
+// Running maximum over each head's tile maxima (prefix scales), in place.
+// Maxima are non-negative binary32 stored as bits, so unsigned order is their
+// order.  One thread per head.
+__global__ void k_prefix_max(uint32_t* __restrict__ amax, int32_t nheads, int32_t ntile) {
+  const int32_t h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= nheads) return;
+  uint32_t* a = amax + static_cast<int64_t>(h) * ntile;
+  uint32_t m = 0;
+  for (int32_t t = 0; t < ntile; ++t) {
+    m = max(m, a[t]);
+    a[t] = m;
+  }
+}
+
 __device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, float cd, float& inv, float& desc) {
   const float A = __uint_as_float(abits);
   if (A == 0.0f) { inv = 1.0f; desc = 1.0f; return; }
@@ -447,6 +461,10 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
       k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, nt, amax_k, a.status);
   }
   k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, 1, amax_v, a.status);
+  if (a.prefix) {
+    k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
+    k_prefix_max<<<dim3((B * hkv + 255) / 256), blk, 0, st>>>(amax_k, B * hkv, nt);
+  }
   if (a.rotate) {
     k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, a.q_desc, a.q8);
     if (a.center)

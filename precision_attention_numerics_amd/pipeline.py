@@ -49,14 +49,16 @@ class AttnPipeline:
                         torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev), tiles)
 
     def prepare(self, q, k, v, rotate: bool, center: bool, signs=None, prep: Prepared | None = None,
-                stream=None, tiles: bool = False) -> Prepared:
+                stream=None, tiles: bool = False, prefix: bool = False) -> Prepared:
         """tiles: one Q/K scale per 128-token tile (FP8A_TILE_SCALES); the
-        forward then uses fp8_attn_fwd_tile_scaled."""
+        forward then uses fp8_attn_fwd_tile_scaled.  prefix (with tiles, not
+        with center): tile t scaled by the largest maximum of tiles 0..t
+        (FP8A_PREFIX_SCALES)."""
         prep = prep or self.alloc_prepared(tiles)
         if prep.tiles != tiles:
             raise ValueError("prepared buffers were allocated for the other scale granularity")
         flags = ((_abi.FP8A_ROTATE_QK if rotate else 0) | (_abi.FP8A_CENTER_K if center else 0)
-                 | (_abi.FP8A_TILE_SCALES if tiles else 0))
+                 | (_abi.FP8A_TILE_SCALES if tiles else 0) | (_abi.FP8A_PREFIX_SCALES if prefix else 0))
         shape = _abi.make_shape(self.B, self.hq, self.hkv, self.N, self.d, q, k, v)
         ws = self._workspace("prep", _abi.prepare_workspace_bytes(shape, flags))
         _abi.fp8_attn_prepare(shape, q, k, v, flags, signs if rotate else None, prep.q8, prep.k8, prep.v8t,

@@ -99,8 +99,10 @@ def test_prepare_rejects(abi):
     assert _prep(abi, abi.make_shape(0, 2, 1, 64, 64)) == -2          # batch
     assert _prep(abi, abi.make_shape(1, 2, 1, 0, 64)) == -2           # seqlen
     assert _prep(abi, ok, dtype=2) == -3                               # f64 input
-    assert _prep(abi, ok, flags=8) == -4                               # unknown flag
+    assert _prep(abi, ok, flags=16) == -4                              # unknown flag
     assert _prep(abi, ok, flags=abi.FP8A_TILE_SCALES, ws_bytes=1) == -5   # tile maxima need workspace too
+    assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES) == -4                # prefix scales need tiles
+    assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES | abi.FP8A_TILE_SCALES | abi.FP8A_CENTER_K) == -3
     assert _prep(abi, ok, q=None) == -1
     assert _prep(abi, ok, flags=abi.FP8A_ROTATE_QK, signs=None) == -1
     assert _prep(abi, ok, ws=None) == -5

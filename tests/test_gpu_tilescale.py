@@ -22,7 +22,7 @@ def pan():
     return pan
 
 
-def run_tiles(pan, w, cond, p_scale=256.0, kv_order=1, block_n=128, causal=True, rows=None):
+def run_tiles(pan, w, cond, p_scale=256.0, kv_order=1, block_n=128, causal=True, rows=None, prefix=False):
     flags = synth.CONDITIONS[cond]
     B, hq, N, d = w.q.shape
     hkv = w.k.shape[1]
@@ -30,8 +30,8 @@ def run_tiles(pan, w, cond, p_scale=256.0, kv_order=1, block_n=128, causal=True,
     print(f"tiles {w.name} {cond} S={p_scale} order={kv_order} bc={block_n} causal={causal} shape={w.q.shape}",
           flush=True)
     gp = pipe.prepare(dev(w.q, w.dtype), dev(w.k, w.dtype), dev(w.v, w.dtype), signs=signs_dev(w), tiles=True,
-                      **flags)
-    op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=True, **flags)
+                      prefix=prefix, **flags)
+    op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=True, prefix=prefix, **flags)
     torch.cuda.synchronize()
     compare_prepared(gp, op, N, flags["center"])
     kw = dict(p_scale=p_scale, kv_order=kv_order, block_n=block_n, causal=causal)
@@ -89,6 +89,38 @@ def test_tiles_of_very_different_magnitude(pan, causal):
         w.k[:, :, 128 * t:128 * (t + 1)] *= np.float32(gains[(t + 1) % 4])
     for cond in ("plain", "rotated"):
         run_tiles(pan, w, cond, causal=causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("cond", ["plain", "rotated"])
+def test_prefix_scales(pan, d, cond):
+    """Prefix tile scales (tile t from the largest maximum of tiles 0..t) on
+    tiles of rising and falling magnitude."""
+    w = synth.qwen_like(1, 4, 2, d, seed=570 + d, N=650, texts=1)
+    gains = (0.5, 4.0, 1.0, 0.25, 8.0, 2.0)
+    for t in range(6):
+        w.q[:, :, 128 * t:128 * (t + 1)] *= np.float32(gains[t])
+        w.k[:, :, 128 * t:128 * (t + 1)] *= np.float32(gains[(t + 2) % 6])
+    run_tiles(pan, w, cond, prefix=True)
+    run_tiles(pan, w, cond, kv_order=0, block_n=64, causal=False, prefix=True)
+
+
+def test_prefix_scales_ignore_future_tokens(pan):
+    """Changing tokens from tile 2 on leaves tiles 0 and 1's codes and scales
+    as they were."""
+    import precision_attention_numerics_amd as pan_
+    w = synth.qwen_like(1, 2, 1, 128, seed=580, N=512, texts=1)
+    pipe = pan_.AttnPipeline(1, 2, 1, 512, 128)
+    args = dict(rotate=True, center=False, signs=signs_dev(w), tiles=True, prefix=True)
+    a = pipe.prepare(dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), **args)
+    q2, k2 = w.q.copy(), w.k.copy()
+    q2[:, :, 256:] *= np.float32(8.0)
+    k2[:, :, 300:] += np.float32(5.0)
+    b = pipe.prepare(dev(q2, "bf16"), dev(k2, "bf16"), dev(w.v, "bf16"), **args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.q8[:, :, :256], b.q8[:, :, :256]) and torch.equal(a.k8[:, :, :256], b.k8[:, :, :256])
+    qa, qb = a.q_desc.view(2, 4), b.q_desc.view(2, 4)
+    assert torch.equal(qa[:, :2], qb[:, :2]) and torch.equal(a.k_desc[:2], b.k_desc[:2])
 
 
 def test_equal_tile_maxima_match_the_per_head_kernel(pan):
