@@ -45,8 +45,9 @@ ROTATE = 1
 CENTER = 2
 TILE = 4
 PREFIX = 8
+INT8 = 16
 TILE_TOKENS = 128
-SCORE_MODES = {"mfma": 0, "exact": 1}
+SCORE_MODES = {"mfma": 0, "exact": 1, "int8": 2}
 
 _c_f32p = ctypes.POINTER(ctypes.c_float)
 _c_f64p = ctypes.POINTER(ctypes.c_double)
@@ -71,6 +72,8 @@ def _load():
     lib.orc_fp8_dot128.argtypes = [_c_u8p, _c_u8p, ctypes.c_int]
     lib.orc_fp8_dot128.restype = ctypes.c_float
     lib.orc_fwht_row.argtypes = [_c_f32p, _c_i8p, _i64]
+    lib.orc_i8_encode.argtypes = [ctypes.c_float]
+    lib.orc_i8_encode.restype = ctypes.c_int8
     lib.orc_attention_f64.argtypes = [_c_f64p, _c_f64p, _c_f64p, _i64, _i64, _i64, _i64, _i64,
                                       ctypes.c_int, ctypes.c_double, _c_i32p, _i64, _c_f64p, ctypes.c_int]
     lib.orc_prepare.argtypes = [_c_f32p, _c_f32p, _c_f32p, _i64, _i64, _i64, _i64, _i64, ctypes.c_uint32,
@@ -118,6 +121,13 @@ def e4m3_encode(x) -> np.ndarray:
     out = np.empty(x.shape, np.uint8)
     _load().orc_e4m3_encode_n(_p(x.reshape(-1), _c_f32p), _p(out.reshape(-1), _c_u8p), x.size)
     return out
+
+
+def i8_encode(x) -> np.ndarray:
+    """int8 codes of binary32 values: round to nearest even, clamp to +-127."""
+    x = np.asarray(x, dtype=np.float32)
+    lib = _load()
+    return np.array([lib.orc_i8_encode(float(v)) for v in x.ravel()], np.int8).reshape(x.shape)
 
 
 def e4m3_decode(c) -> np.ndarray:
@@ -200,16 +210,18 @@ class Prepared:
     v_desc: np.ndarray
     k_mean: np.ndarray | None
     tiles: bool = False     # q_desc [B,Hq,T] / k_desc [B,Hkv,T] per 128-token tile
+    int8: bool = False      # Q/K codes are int8 (scores: exact integer dot)
 
 
 def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, tiles: bool = False,
-            prefix: bool = False) -> Prepared:
+            prefix: bool = False, int8: bool = False) -> Prepared:
     """Quantisation prologue on binary32 operands (BF16 widened exactly).
     tiles: one Q/K scale per 128-token tile instead of per (batch, head) (the
     earlier emulator's granularity, attention-numerics project page, second
     section); V keeps per-head scales.  prefix (with tiles, without center):
     tile t's Q/K scale from the largest maximum among tiles 0..t, so no scale
-    depends on tokens past its tile."""
+    depends on tokens past its tile.  int8: Q/K as int8 codes (scale 127/A,
+    round to nearest even, clamp +-127), V still E4M3."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     v = np.ascontiguousarray(v, dtype=np.float32)
@@ -225,16 +237,16 @@ def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, til
     vd = np.empty(B * Hkv, np.float32)
     km = np.empty(B * Hkv * d, np.float32) if center else None
     flags = ((ROTATE if rotate else 0) | (CENTER if center else 0) | (TILE if tiles else 0)
-             | (PREFIX if prefix else 0))
+             | (PREFIX if prefix else 0) | (INT8 if int8 else 0))
     rc = _load().orc_prepare(_p(q, _c_f32p), _p(k, _c_f32p), _p(v, _c_f32p), B, Hq, Hkv, N, d, flags,
                              _p(s, _c_i8p), _p(q8, _c_u8p), _p(k8, _c_u8p), _p(v8, _c_u8p),
                              _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p), _p(km, _c_f32p))
     _check(rc, "prepare")
     if tiles:
         return Prepared(q8, k8, v8, qd.reshape(B, Hq, T), kd.reshape(B, Hkv, T), vd.reshape(B, Hkv),
-                        None if km is None else km.reshape(B, Hkv, d), True)
+                        None if km is None else km.reshape(B, Hkv, d), True, int8)
     return Prepared(q8, k8, v8, qd.reshape(B, Hq), kd.reshape(B, Hkv), vd.reshape(B, Hkv),
-                    None if km is None else km.reshape(B, Hkv, d))
+                    None if km is None else km.reshape(B, Hkv, d), False, int8)
 
 
 @dataclass
@@ -263,6 +275,8 @@ def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: f
     kd = np.ascontiguousarray(prep.k_desc, np.float32)
     vd = np.ascontiguousarray(prep.v_desc, np.float32)
     fn = _load().orc_attention_fp8_tiles if prep.tiles else _load().orc_attention_fp8
+    if prep.int8:
+        score_mode = "int8"
     rc = fn(_p(prep.q8, _c_u8p), _p(prep.k8, _c_u8p), _p(prep.v8, _c_u8p),
             _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p),
             B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale), int(kv_order),

@@ -56,10 +56,18 @@ static float column_mean(const float* K, int64_t N, int64_t d, int64_t c, double
   return (float)(part[0] / (double)N);
 }
 
-static void scales_from_amax(float A, int rotated, int64_t d, float* inv, float* desc) {
+int8_t orc_i8_encode(float x) {
+  float r = rintf(x);  /* the default rounding mode: to nearest, ties to even */
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
+}
+
+/* qmax: the largest code magnitude, 448 for E4M3 and 127 for int8. */
+static void scales_from_amax(float A, int rotated, int64_t d, float qmax, float* inv, float* desc) {
   if (A == 0.0f) { *inv = 1.0f; *desc = 1.0f; return; }
-  *inv = 448.0f / A;
-  *desc = A / 448.0f;
+  *inv = qmax / A;
+  *desc = A / qmax;
   if (rotated) *desc = *desc * (float)(1.0 / sqrt((double)d));
 }
 
@@ -71,7 +79,7 @@ int orc_prepare(const float* q, const float* k, const float* v,
   if (!q || !k || !v || !q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc) return -1;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv || (d & (d - 1))) return -1;
   int rotate = (flags & ORC_ROTATE) != 0, center = (flags & ORC_CENTER) != 0;
-  int tiled = (flags & ORC_TILE) != 0, prefix = (flags & ORC_PREFIX) != 0;
+  int tiled = (flags & ORC_TILE) != 0, prefix = (flags & ORC_PREFIX) != 0, i8 = (flags & ORC_INT8) != 0;
   if (prefix && (!tiled || center)) return -1;
   /* scale groups: the whole sequence, or 128-token tiles */
   int64_t span = tiled ? ORC_TILE_TOKENS : N, ngroup = (N + span - 1) / span;
@@ -84,6 +92,7 @@ int orc_prepare(const float* q, const float* k, const float* v,
   float* buf = (float*)malloc(sizeof(float) * (size_t)(N * d));
   if (!part || !row || !mu || !buf) { free(part); free(row); free(mu); free(buf); return -3; }
 
+  const float qk_max = i8 ? 127.0f : 448.0f;
   /* Q: rotate, amax per scale group, quantise. */
   for (int64_t bh = 0; bh < B * Hq; ++bh) {
     const float* src = q + bh * N * d;
@@ -98,9 +107,10 @@ int orc_prepare(const float* q, const float* k, const float* v,
       for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
       if (prefix) { if (A > Apre) Apre = A; A = Apre; }
       float inv, desc;
-      scales_from_amax(A, rotate, d, &inv, &desc);
+      scales_from_amax(A, rotate, d, qk_max, &inv, &desc);
       q_desc[bh * ngroup + t] = desc;
-      for (int64_t e = e0; e < e1; ++e) q8[bh * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+      for (int64_t e = e0; e < e1; ++e)
+        q8[bh * N * d + e] = i8 ? (uint8_t)orc_i8_encode(buf[e] * inv) : orc_e4m3_encode(buf[e] * inv);
     }
   }
   /* K: centre, rotate, amax, quantise.  V: amax, quantise (never rotated). */
@@ -118,15 +128,16 @@ int orc_prepare(const float* q, const float* k, const float* v,
       A = 0.0f;
       for (int64_t e = e0; e < e1; ++e) { float a = fabsf(buf[e]); if (a > A) A = a; }
       if (prefix) { if (A > Apre) Apre = A; A = Apre; }
-      scales_from_amax(A, rotate, d, &inv, &desc);
+      scales_from_amax(A, rotate, d, qk_max, &inv, &desc);
       k_desc[bg * ngroup + t] = desc;
-      for (int64_t e = e0; e < e1; ++e) k8[bg * N * d + e] = orc_e4m3_encode(buf[e] * inv);
+      for (int64_t e = e0; e < e1; ++e)
+        k8[bg * N * d + e] = i8 ? (uint8_t)orc_i8_encode(buf[e] * inv) : orc_e4m3_encode(buf[e] * inv);
     }
 
     const float* vs = v + bg * N * d;
     A = 0.0f;
     for (int64_t e = 0; e < N * d; ++e) { float a = fabsf(vs[e]); if (a > A) A = a; }
-    scales_from_amax(A, 0, d, &inv, &desc);
+    scales_from_amax(A, 0, d, 448.0f, &inv, &desc);  /* V is always E4M3 */
     v_desc[bg] = desc;
     for (int64_t e = 0; e < N * d; ++e) v8[bg * N * d + e] = orc_e4m3_encode(vs[e] * inv);
   }
@@ -271,7 +282,13 @@ static void attn_row(void* p, int64_t item, double* scratch) {
   for (int64_t j = 0; j < nvis; ++j) {
     if (fp8) {
       memcpy(kpad, a->k8 + (bg * N + j) * d, (size_t)d);
-      s[j] = orc_fp8_dot128(qpad, kpad, a->score_mode);
+      if (a->score_mode == 2) { /* int8 codes: exact integer dot */
+        int64_t t = 0;
+        for (int64_t cc = 0; cc < d; ++cc) t += (int64_t)(int8_t)qpad[cc] * (int64_t)(int8_t)kpad[cc];
+        s[j] = (double)(float)t;
+      } else {
+        s[j] = orc_fp8_dot128(qpad, kpad, a->score_mode);
+      }
     } else { /* ordered binary32 fused multiply-add chain over the channels */
       const float* qr = a->qf + (bh * N + i) * d;
       const float* kr = a->kf + (bg * N + j) * d;

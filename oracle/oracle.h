@@ -34,6 +34,16 @@
  * the caveat the project page raises about full-sequence scales).  Not
  * combined with CENTER (one K code set cannot carry a per-query prefix mean). */
 #define ORC_PREFIX 8u
+/* INT8 Q/K (the INT8-QK / FP8-PV kernel family the attention-numerics project
+ * page measures, named without its quantisation): Q and K codes are
+ * two's-complement int8 = clamp(RNE(x * 127/A), -127, 127) with the same scale
+ * groups, descale A/127 (times RN32(1/sqrt d) when rotated); V stays E4M3.
+ * The score of two int8 rows is their exact integer dot product (|s| <=
+ * 127^2 * 128 < 2^24, exact in binary32): orc_attention_fp8 with score_mode 2. */
+#define ORC_INT8 16u
+
+/* int8 code of a binary32 value: round to nearest even, clamp to +-127. */
+int8_t orc_i8_encode(float x);
 
 /* E4M3FN codec: round to nearest, ties to even, saturating at +-448. */
 uint8_t orc_e4m3_encode(float x);
