@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-scales", action="store_true",
                     help="one Q/K scale per 128-token tile (the variant) instead of per (batch, head)")
+    ap.add_argument("--int8-qk", action="store_true",
+                    help="Q/K as int8 codes with exact integer scores (the INT8-QK / FP8-PV variant)")
     ap.add_argument("--sample-tiles", type=int, default=3, help="query tiles per head in the CPU sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy (read + write of this many MiB), for scaling HBM counters")
@@ -131,7 +133,7 @@ def main():
         for cond in ("centered_rotated", "rotated"):
             fl = synth.CONDITIONS[cond]
             ta = time.perf_counter()
-            op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=args.tile_scales, **fl)
+            op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=args.tile_scales, int8=args.int8_qk, **fl)
             emu = oracle.attention_fp8(op, p_scale=256.0, kv_order=1, block_n=128, causal=True, rows=rows)
             tb = time.perf_counter()
             if cond == "centered_rotated":
@@ -149,7 +151,7 @@ def main():
                           f"binary64 reference on the same rows {t_ideal:.1f}s")}
 
     ref = torch.from_numpy(ref_rows["f64"]).cuda() if ref_rows else torch.zeros((B, hq, rows.size, d), dtype=torch.float64, device="cuda")
-    prep = pipe.alloc_prepared(args.tile_scales)
+    prep = pipe.alloc_prepared(args.tile_scales, args.int8_qk)
     out = torch.empty((B, hq, N, d), dtype=torch.float32, device="cuda")
     rel = torch.empty(B * hq, dtype=torch.float64, device="cuda")
 
@@ -157,7 +159,7 @@ def main():
         fl = synth.CONDITIONS[cond]
         if ev is not None:
             ev[0].record()
-        pipe.prepare(q, k, v, signs=signs, prep=prep, tiles=args.tile_scales, **fl)
+        pipe.prepare(q, k, v, signs=signs, prep=prep, tiles=args.tile_scales, int8=args.int8_qk, **fl)
         if ev is not None:
             ev[1].record()
         pipe.fwd(prep, p_scale=256.0, kv_order=1, block_n=128, causal=True, out=out)
@@ -214,12 +216,14 @@ def main():
                                "BF16 sink-generator operands (Delta=8, 4 sinks), S=256, reverse KV order, block 128" % N,
                    "condition": "centered_rotated",
                    "qk_scales": "per 128-token tile" if args.tile_scales else "per (batch, head)",
+                   "qk_codes": "int8" if args.int8_qk else "e4m3",
                    "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": (None if args.tile_scales else
-                                 profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false, false>")),
-                     "kernel": "k_attn_fwd<128,128,2,causal,pow2%s>" % (",tiles" if args.tile_scales else ""),
+                     "traffic": (None if (args.tile_scales or args.int8_qk) else
+                                 profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false, false, false>")),
+                     "kernel": "k_attn_fwd<128,128,2,causal,pow2%s%s>" % (",tiles" if args.tile_scales else "",
+                                                                         ",int8qk" if args.int8_qk else ""),
                      "flop_per_launch": flop},
         "cpu_baseline": cpu,
         "detail": results,

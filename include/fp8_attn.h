@@ -40,7 +40,7 @@ typedef enum {
   FP8A_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 } fp8a_status;
 
-typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3 } fp8a_dtype;
+typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3, FP8A_I8QK = 4 } fp8a_dtype;
 
 /* Prologue flags.  ROTATE: fixed random-sign Hadamard on Q and K, never V
  * (attention-numerics study page, "See the vectors and the arithmetic").
@@ -61,6 +61,13 @@ typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3 } fp8a_d
  * Errors: FP8A_ERR_PARAM without TILE_SCALES, FP8A_ERR_UNSUPPORTED with
  * CENTER_K (one set of K codes cannot carry a per-query prefix mean). */
 #define FP8A_PREFIX_SCALES 8u
+/* INT8_QK: Q and K become two's-complement int8 codes, clamp(RNE(x * 127/A),
+ * -127, 127), with descale A/127 (times RN32(1/sqrt d) when rotated); V stays
+ * E4M3.  This is the INT8-QK / FP8-PV kernel family the project page measures
+ * besides FA3 (SageAttention); the pages give none of its quantisation, so the
+ * scale groups are FA3's per (batch, head).  Such codes go to fp8_attn_fwd with
+ * qkv_dtype FP8A_I8QK.  Not combined with TILE_SCALES (FP8A_ERR_UNSUPPORTED). */
+#define FP8A_INT8_QK 16u
 
 typedef struct {
   int32_t batch;     /* B >= 1 */
@@ -135,6 +142,8 @@ int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
  * Arguments
  *   qkv_dtype  FP8A_E4M3: q = q8 [B,hq,Np,d], k = k8 [B,hkv,Np,d], v = v8t
  *              [B,hkv,d,Np] as written by fp8_attn_prepare, descales required.
+ *              FP8A_I8QK: the same with int8 q and k codes (an INT8_QK
+ *              prologue); the score is their exact integer dot product.
  *              FP8A_F32: dense binary32 q/k/v [B,h,N,d], only P is cast
  *              ("kernel-faithful" simulation of the P-Cast summary, Bijdragen
  *              item 4); scores are an ordered binary32 fma chain over the

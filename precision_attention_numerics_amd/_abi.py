@@ -17,8 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8attn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8_attn.h")
 
-FP8A_F32, FP8A_BF16, FP8A_F64, FP8A_E4M3 = 0, 1, 2, 3
-FP8A_ROTATE_QK, FP8A_CENTER_K, FP8A_TILE_SCALES, FP8A_PREFIX_SCALES = 1, 2, 4, 8
+FP8A_F32, FP8A_BF16, FP8A_F64, FP8A_E4M3, FP8A_I8QK = 0, 1, 2, 3, 4
+FP8A_ROTATE_QK, FP8A_CENTER_K, FP8A_TILE_SCALES, FP8A_PREFIX_SCALES, FP8A_INT8_QK = 1, 2, 4, 8, 16
 STATUS = {0: "FP8A_OK", -1: "FP8A_ERR_NULL", -2: "FP8A_ERR_SHAPE", -3: "FP8A_ERR_UNSUPPORTED",
           -4: "FP8A_ERR_PARAM", -5: "FP8A_ERR_WORKSPACE", -6: "FP8A_ERR_HIP"}
 

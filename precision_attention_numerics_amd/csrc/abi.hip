@@ -106,7 +106,9 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   int rc = check_shape(s);
   if (rc) return rc;
   if (in_dtype != FP8A_F32 && in_dtype != FP8A_BF16) return FP8A_ERR_UNSUPPORTED;
-  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K | FP8A_TILE_SCALES | FP8A_PREFIX_SCALES)) return FP8A_ERR_PARAM;
+  if (flags & ~(FP8A_ROTATE_QK | FP8A_CENTER_K | FP8A_TILE_SCALES | FP8A_PREFIX_SCALES | FP8A_INT8_QK))
+    return FP8A_ERR_PARAM;
+  if ((flags & FP8A_INT8_QK) && (flags & FP8A_TILE_SCALES)) return FP8A_ERR_UNSUPPORTED;
   if ((flags & FP8A_PREFIX_SCALES) && !(flags & FP8A_TILE_SCALES)) return FP8A_ERR_PARAM;
   if ((flags & FP8A_PREFIX_SCALES) && (flags & FP8A_CENTER_K)) return FP8A_ERR_UNSUPPORTED;
   if (!q || !k || !v || !q8 || !k8 || !v8t || !q_desc || !k_desc || !v_desc) return FP8A_ERR_NULL;
@@ -127,6 +129,7 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   a.center = (flags & FP8A_CENTER_K) != 0;
   a.ntile = (flags & FP8A_TILE_SCALES) ? a.Np / 128 : 1;
   a.prefix = (flags & FP8A_PREFIX_SCALES) != 0;
+  a.int8 = (flags & FP8A_INT8_QK) != 0;
   a.q = q; a.k = k; a.v = v;
   a.signs = rot_signs;
   a.cd = static_cast<float>(1.0 / sqrt(static_cast<double>(s->head_dim)));
@@ -157,15 +160,15 @@ int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const v
                bool tiles) {
   int rc = check_shape(s);
   if (rc) return rc;
-  if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32) return FP8A_ERR_UNSUPPORTED;
+  if (qkv_dtype != FP8A_E4M3 && qkv_dtype != FP8A_F32 && qkv_dtype != FP8A_I8QK) return FP8A_ERR_UNSUPPORTED;
   if (tiles && qkv_dtype != FP8A_E4M3) return FP8A_ERR_UNSUPPORTED;
+  const bool codes = qkv_dtype == FP8A_E4M3 || qkv_dtype == FP8A_I8QK;
   if (!q || !k || !v || !out) return FP8A_ERR_NULL;
   // the E4M3 kernel addresses one head's K8 / V8t through a buffer resource
   // with a 31-bit byte range
-  if (qkv_dtype == FP8A_E4M3 &&
-      static_cast<int64_t>(fp8_attn_padded_seqlen(s->seqlen)) * s->head_dim > INT32_MAX)
+  if (codes && static_cast<int64_t>(fp8_attn_padded_seqlen(s->seqlen)) * s->head_dim > INT32_MAX)
     return FP8A_ERR_SHAPE;
-  if (qkv_dtype == FP8A_E4M3 && (!q_desc || !k_desc || !v_desc)) return FP8A_ERR_NULL;
+  if (codes && (!q_desc || !k_desc || !v_desc)) return FP8A_ERR_NULL;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return FP8A_ERR_PARAM;
   if (!(p_scale > 0.0f) || !(p_scale <= 448.0f)) return FP8A_ERR_PARAM;
   if (kv_order != 0 && kv_order != 1) return FP8A_ERR_PARAM;
@@ -197,6 +200,7 @@ int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const v
   p.B = s->batch; p.hq = s->hq; p.hkv = s->hkv; p.N = s->seqlen; p.Np = fp8_attn_padded_seqlen(s->seqlen);
   p.n_qtiles = p.Np / 128; p.kv_order = kv_order; p.k_sink = k_sink;
   p.tiles = tiles ? 1 : 0;
+  p.int8 = qkv_dtype == FP8A_I8QK ? 1 : 0;
   p.ls2 = ls2; p.S = p_scale; p.inv_S = inv_S; p.bad0 = bad0; p.bad1 = bad1;
   {
     float x0, x1;

@@ -19,6 +19,7 @@ struct FwdParams {
   uint32_t* row_zeros;    // [B,hq,N] or null
   int32_t B, hq, hkv, N, Np, n_qtiles, kv_order, k_sink;
   int32_t tiles;          // 1: q_desc [B*hq*n_qtiles], k_desc [B*hkv*n_qtiles] per 128-token tile
+  int32_t int8;           // 1: q8 / k8 hold int8 codes (exact integer scores)
   float ls2;              // RN32(softmax_scale * log2 e)
   float S;                // static P scale
   float inv_S;            // 1/S when S is a power of two

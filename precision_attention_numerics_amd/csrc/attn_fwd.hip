@@ -43,6 +43,19 @@ __device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// 16x16x64 int8 with exact int32 accumulation: A lane l = row l%16, bytes =
+// k 16*(l/16) + [0, 16); B likewise by column; D as the 16x16 forms.
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4i lds_read16_i(const uint8_t* p) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  return v4i{static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3])};
+}
+
 // p = 2^x in binary32.  v_exp_f32 differs from the correctly rounded 2^x in
 // the last place for some x; exhaustive checks over every binary32 x in
 // [-150, 2^-8] show that for S = 2^k (k = 0..8) only two such x change an E4M3
@@ -323,7 +336,7 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
   return out;
 }
 
-template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP, bool TILES>
+template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP, bool TILES, bool I8>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   constexpr int QROWS = kWaves * QT * 16;
   static_assert(QROWS == 128, "query tile must match the 128-token padding");
@@ -383,12 +396,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
       for (int e = 0; e < 8; ++e) qop[qt][e] = 0;
     }
   }
+  // int8 Q operand: query row n16, channels 64 h + [16 lg, 16 lg + 16)
+  constexpr int NH8 = D / 64;
+  v4i qop8[I8 ? QT : 1][NH8];
+  if constexpr (I8) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int h8 = 0; h8 < NH8; ++h8) {
+        const int i = q0 + wv * QT * 16 + qt * 16 + n16;
+        const uint4 a = *reinterpret_cast<const uint4*>(p.q8 + (static_cast<int64_t>(bh) * Np + i) * D + 64 * h8 + 16 * lg);
+        qop8[qt][h8] = v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w)};
+      }
+  }
 
   // ---- per-lane LDS read offsets (tile t / channel tile ct add constants)
   // K: A row m = n16 of tile t -> key KPL*(m/4) + 4t + m%4 = LDS row 16t + n16,
   // channels [32 lg, 32 lg + 32)
   const int kofs0 = 16 * (n16 * UK + ((2 * lg) ^ swz<UK>(n16)));
   const int kofs1 = 16 * (n16 * UK + ((2 * lg + 1) ^ swz<UK>(n16)));
+  // int8 K operand: channels 64 h + [16 lg, 16 lg + 16) = unit 4 h + lg
+  int kofs8[NH8];
+#pragma unroll
+  for (int h8 = 0; h8 < NH8; ++h8) kofs8[h8] = 16 * (n16 * UK + ((4 * h8 + lg) ^ swz<UK>(n16)));
   // V^T: A row = channel 16 ct + n16, keys [KPL lg, KPL lg + KPL)
   const int vofs0 = 16 * (n16 * UV + ((KPL == 32 ? 2 * lg : lg) ^ swz<UV>(n16)));
   const int vofs1 = 16 * (n16 * UV + ((2 * lg + 1) ^ swz<UV>(n16)));
@@ -440,15 +470,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
     v4f sall[QT][T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      v8i a;
-      if (has_k) {
-        a = lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK);
+      if constexpr (I8) {
+        // exact int32 scores, converted once (|s| <= 127^2 * 128 < 2^24)
+        v4i a8[NH8];
+#pragma unroll
+        for (int h8 = 0; h8 < NH8; ++h8) a8[h8] = lds_read16_i(kt + kofs8[h8] + t * 256 * UK);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int h8 = 0; h8 < NH8; ++h8) acc = mfma_i8(a8[h8], qop8[qt][h8], acc);
+          sall[qt][t] = v4f{static_cast<float>(acc[0]), static_cast<float>(acc[1]), static_cast<float>(acc[2]),
+                            static_cast<float>(acc[3])};
+        }
       } else {
+        v8i a;
+        if (has_k) {
+          a = lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = 0;
+          for (int e = 0; e < 8; ++e) a[e] = 0;
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sall[qt][t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
       }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) sall[qt][t] = mfma_f8(a, qop[qt], v4f{0.0f, 0.0f, 0.0f, 0.0f});
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -582,8 +627,9 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
 template <int D, int BC, bool CAUSAL, bool POW2, bool DUMP>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.B * p.hq * p.n_qtiles));
-  if (p.tiles) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, true><<<grid, dim3(kThreads), 0, st>>>(p);
-  else k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false><<<grid, dim3(kThreads), 0, st>>>(p);
+  if (p.tiles) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, true, false><<<grid, dim3(kThreads), 0, st>>>(p);
+  else if (p.int8) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false, true><<<grid, dim3(kThreads), 0, st>>>(p);
+  else k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false, false><<<grid, dim3(kThreads), 0, st>>>(p);
   return hipGetLastError();
 }
 

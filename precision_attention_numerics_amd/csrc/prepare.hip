@@ -299,11 +299,24 @@ __global__ void k_prefix_max(uint32_t* __restrict__ amax, int32_t nheads, int32_
   }
 }
 
-__device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, float cd, float& inv, float& desc) {
+// int8 code: round to nearest even (v_rndne_f32), clamp to +-127, two's
+// complement byte; four of them packed little-endian.
+__device__ __forceinline__ uint32_t i8_code(float x) {
+  const float r = __builtin_fminf(127.0f, __builtin_fmaxf(-127.0f, __builtin_rintf(x)));
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t i8_pack4(float a, float b, float c, float d) {
+  return i8_code(a) | (i8_code(b) << 8) | (i8_code(c) << 16) | (i8_code(d) << 24);
+}
+
+// qmax: the largest code magnitude, 448 for E4M3 and 127 for int8 codes.
+__device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, float cd, float& inv, float& desc,
+                                                 float qmax = 448.0f) {
   const float A = __uint_as_float(abits);
   if (A == 0.0f) { inv = 1.0f; desc = 1.0f; return; }
-  inv = 448.0f / A;
-  desc = A / 448.0f;
+  inv = qmax / A;
+  desc = A / qmax;
   if (rotated) desc = desc * cd;
 }
 
@@ -314,7 +327,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
                                                              int32_t H, int32_t N, int32_t Np, const float* __restrict__ mu_all,
                                                              int32_t hq_per_mu, const int8_t* __restrict__ signs,
                                                              int32_t ntile, const uint32_t* __restrict__ amax, float cd,
-                                                             float* __restrict__ desc_out, uint8_t* __restrict__ codes) {
+                                                             int32_t int8, float* __restrict__ desc_out,
+                                                             uint8_t* __restrict__ codes) {
+  const float qmax = int8 ? 127.0f : 448.0f;
   constexpr int L = D / 8;
   constexpr int RPI = kPrepThreads / L;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -324,15 +339,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
   // scales of the block's rows [0, 128) and [128, 256)
   float inv, desc, inv_hi, desc_hi;
   if (ntile == 1) {
-    scales_from_amax(amax[bh], ROT, cd, inv, desc);
+    scales_from_amax(amax[bh], ROT, cd, inv, desc, qmax);
     inv_hi = inv;
     desc_hi = desc;
     if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
   } else {
     const int64_t t0 = static_cast<int64_t>(bh) * ntile + 2 * blockIdx.x;
     const bool has_hi = n_begin + kRowsPerBlock / 2 < Np;   // the block's second tile exists
-    scales_from_amax(amax[t0], ROT, cd, inv, desc);
-    scales_from_amax(has_hi ? amax[t0 + 1] : 0u, ROT, cd, inv_hi, desc_hi);
+    scales_from_amax(amax[t0], ROT, cd, inv, desc, qmax);
+    scales_from_amax(has_hi ? amax[t0 + 1] : 0u, ROT, cd, inv_hi, desc_hi, qmax);
     if (threadIdx.x == 0) desc_out[t0] = desc;
     if (threadIdx.x == 1 && has_hi) desc_out[t0 + 1] = desc_hi;
   }
@@ -361,10 +376,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
       if (n < N) {
         const float s = (r0 + u * RPI < kRowsPerBlock / 2) ? inv : inv_hi;
         uint32_t lo = 0, hi = 0;
-        lo = e4m3_pack2<false>(v[u][0] * s, v[u][1] * s, lo);
-        lo = e4m3_pack2<true>(v[u][2] * s, v[u][3] * s, lo);
-        hi = e4m3_pack2<false>(v[u][4] * s, v[u][5] * s, hi);
-        hi = e4m3_pack2<true>(v[u][6] * s, v[u][7] * s, hi);
+        if (int8) {
+          lo = i8_pack4(v[u][0] * s, v[u][1] * s, v[u][2] * s, v[u][3] * s);
+          hi = i8_pack4(v[u][4] * s, v[u][5] * s, v[u][6] * s, v[u][7] * s);
+        } else {
+          lo = e4m3_pack2<false>(v[u][0] * s, v[u][1] * s, lo);
+          lo = e4m3_pack2<true>(v[u][2] * s, v[u][3] * s, lo);
+          hi = e4m3_pack2<false>(v[u][4] * s, v[u][5] * s, hi);
+          hi = e4m3_pack2<true>(v[u][6] * s, v[u][7] * s, hi);
+        }
         w = make_uint2(lo, hi);
       }
       // rows in [N, Np) are written as zero codes
@@ -466,17 +486,17 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
     k_prefix_max<<<dim3((B * hkv + 255) / 256), blk, 0, st>>>(amax_k, B * hkv, nt);
   }
   if (a.rotate) {
-    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, a.q_desc, a.q8);
+    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, a.int8 ? 1 : 0, a.q_desc, a.q8);
     if (a.center)
-      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, nt, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
     else
-      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, nt, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
   } else {
-    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, a.q_desc, a.q8);
+    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, a.int8 ? 1 : 0, a.q_desc, a.q8);
     if (a.center)
-      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
     else
-      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, a.k_desc, a.k8);
+      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
   }
   k_quant_vt<IT, D><<<dim3(Np / 128, B * hkv), blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, Np, amax_v, a.v_desc, a.v8t);
   (void)grp;

@@ -7,7 +7,7 @@ namespace fp8a {
 
 struct PrepareArgs {
   int32_t B, hq, hkv, N, Np, D;
-  bool bf16, rotate, center, prefix;
+  bool bf16, rotate, center, prefix, int8;
   int32_t ntile;                 // Q/K scale groups per head: Np/128 with per-tile scales, else 1
   const void *q, *k, *v;
   int64_t qs[3], ks[3], vs[3];   // element strides of (batch, head, token)

@@ -21,6 +21,7 @@ class Prepared:
     k_mean: torch.Tensor   # [B*hkv*d] (valid after a centred prepare)
     status: torch.Tensor   # [1] int32
     tiles: bool = False    # Q/K descales per 128-token tile
+    int8: bool = False     # Q/K hold int8 codes (INT8-QK variant)
 
 
 class AttnPipeline:
@@ -38,7 +39,7 @@ class AttnPipeline:
             self._ws[key] = t
         return t
 
-    def alloc_prepared(self, tiles: bool = False) -> Prepared:
+    def alloc_prepared(self, tiles: bool = False, int8: bool = False) -> Prepared:
         B, hq, hkv, Np, d, dev = self.B, self.hq, self.hkv, self.Np, self.d, self.device
         T = Np // 128 if tiles else 1
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -46,19 +47,21 @@ class AttnPipeline:
         return Prepared(torch.empty((B, hq, Np, d), **u8), torch.empty((B, hkv, Np, d), **u8),
                         torch.empty((B, hkv, d, Np), **u8), torch.empty(B * hq * T, **f32),
                         torch.empty(B * hkv * T, **f32), torch.empty(B * hkv, **f32),
-                        torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev), tiles)
+                        torch.zeros(B * hkv * d, **f32), torch.zeros(1, dtype=torch.int32, device=dev), tiles, int8)
 
     def prepare(self, q, k, v, rotate: bool, center: bool, signs=None, prep: Prepared | None = None,
-                stream=None, tiles: bool = False, prefix: bool = False) -> Prepared:
+                stream=None, tiles: bool = False, prefix: bool = False, int8: bool = False) -> Prepared:
         """tiles: one Q/K scale per 128-token tile (FP8A_TILE_SCALES); the
         forward then uses fp8_attn_fwd_tile_scaled.  prefix (with tiles, not
         with center): tile t scaled by the largest maximum of tiles 0..t
-        (FP8A_PREFIX_SCALES)."""
-        prep = prep or self.alloc_prepared(tiles)
-        if prep.tiles != tiles:
-            raise ValueError("prepared buffers were allocated for the other scale granularity")
+        (FP8A_PREFIX_SCALES).  int8: Q/K as int8 codes (FP8A_INT8_QK); the
+        forward then takes qkv_dtype FP8A_I8QK."""
+        prep = prep or self.alloc_prepared(tiles, int8)
+        if prep.tiles != tiles or prep.int8 != int8:
+            raise ValueError("prepared buffers were allocated for another scale granularity or code type")
         flags = ((_abi.FP8A_ROTATE_QK if rotate else 0) | (_abi.FP8A_CENTER_K if center else 0)
-                 | (_abi.FP8A_TILE_SCALES if tiles else 0) | (_abi.FP8A_PREFIX_SCALES if prefix else 0))
+                 | (_abi.FP8A_TILE_SCALES if tiles else 0) | (_abi.FP8A_PREFIX_SCALES if prefix else 0)
+                 | (_abi.FP8A_INT8_QK if int8 else 0))
         shape = _abi.make_shape(self.B, self.hq, self.hkv, self.N, self.d, q, k, v)
         ws = self._workspace("prep", _abi.prepare_workspace_bytes(shape, flags))
         _abi.fp8_attn_prepare(shape, q, k, v, flags, signs if rotate else None, prep.q8, prep.k8, prep.v8t,
@@ -79,7 +82,8 @@ class AttnPipeline:
                                           out, lse=lse, p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros,
                                           k_sink=k_sink, stream=stream)
         else:
-            _abi.fp8_attn_fwd(self.shape, _abi.FP8A_E4M3, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
+            dtype = _abi.FP8A_I8QK if prep.int8 else _abi.FP8A_E4M3
+            _abi.fp8_attn_fwd(self.shape, dtype, prep.q8, prep.k8, prep.v8t, prep.q_desc, prep.k_desc,
                               prep.v_desc, softmax_scale, p_scale, kv_order, block_n, int(causal), out, lse=lse,
                               p_dump=p_dump, row_hash=row_hash, row_zeros=row_zeros, k_sink=k_sink, stream=stream)
         return out

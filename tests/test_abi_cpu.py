@@ -99,10 +99,11 @@ def test_prepare_rejects(abi):
     assert _prep(abi, abi.make_shape(0, 2, 1, 64, 64)) == -2          # batch
     assert _prep(abi, abi.make_shape(1, 2, 1, 0, 64)) == -2           # seqlen
     assert _prep(abi, ok, dtype=2) == -3                               # f64 input
-    assert _prep(abi, ok, flags=16) == -4                              # unknown flag
+    assert _prep(abi, ok, flags=32) == -4                              # unknown flag
     assert _prep(abi, ok, flags=abi.FP8A_TILE_SCALES, ws_bytes=1) == -5   # tile maxima need workspace too
     assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES) == -4                # prefix scales need tiles
     assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES | abi.FP8A_TILE_SCALES | abi.FP8A_CENTER_K) == -3
+    assert _prep(abi, ok, flags=abi.FP8A_INT8_QK | abi.FP8A_TILE_SCALES) == -3         # int8 only per head
     assert _prep(abi, ok, q=None) == -1
     assert _prep(abi, ok, flags=abi.FP8A_ROTATE_QK, signs=None) == -1
     assert _prep(abi, ok, ws=None) == -5
@@ -129,6 +130,8 @@ def test_fwd_rejects(abi):
     assert _fwd(abi, ok, S=0.5) == -3
     assert _fwd(abi, ok, k_sink=-1) == -4
     assert _fwd(abi, ok, dtype=1) == -3                                 # bf16 operands go through prepare
+    assert _fwd(abi, ok, dtype=4, desc=None) == -1                      # int8 Q/K codes need descales too
+    assert _fwd(abi, ok, dtype=5) == -3
     assert _fwd(abi, ok, desc=None) == -1
     assert _fwd(abi, ok, out=None) == -1
     assert _fwd(abi, abi.make_shape(1, 2, 1, 64, 32)) == -2
