@@ -227,22 +227,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x,
   // kRowsInFlight rows per lane group per step, loaded before any is
   // transformed.  Rows past N are not loaded and not counted; the L lanes of a
   // row share r, so the lane exchanges of a row always run on all its lanes.
+  // r0 + u * RPI < kRowsPerBlock always holds (r0 < RPI + 3 * kRowsInFlight * RPI).
+  // Rows past N load row N - 1 instead (no branch around the loads, so all
+  // of them are in flight together) and are not counted.
   for (int r0 = rl; r0 < kRowsPerBlock; r0 += kRowsInFlight * RPI) {
     float v[kRowsInFlight][8];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      const int n = n_begin + r0 + u * RPI;
-      if (r0 + u * RPI < kRowsPerBlock && n < N) {
-        load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
-      }
+      const int n = min(n_begin + r0 + u * RPI, N - 1);
+      load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int n = n_begin + r0 + u * RPI;
-      const bool live = r0 + u * RPI < kRowsPerBlock && n < N;
+      const bool live = n < N;
 #pragma unroll
       for (int e = 0; e < 8; ++e) bad |= live && !__builtin_isfinite(v[u][e]);
       transform_row<D, ROT, CENTER>(v[u], li, mu, signs);
@@ -356,17 +354,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
   // kRowsInFlight rows per lane group per step, loaded before any is
   // transformed (the L lanes of a row share r, so its lane exchanges always run
   // on all of them).
+  // Rows past N load row N - 1 instead (no branch around the loads) and are
+  // written as zero codes.
   for (int r0 = rl; r0 < kRowsPerBlock; r0 += kRowsInFlight * RPI) {
     float v[kRowsInFlight][8];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      const int n = n_begin + r0 + u * RPI;
-      if (r0 + u * RPI < kRowsPerBlock && n < N) {
-        load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
-      }
+      const int n = min(n_begin + r0 + u * RPI, N - 1);
+      load8<IT>(base + static_cast<int64_t>(n) * sn, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
@@ -388,7 +383,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
         w = make_uint2(lo, hi);
       }
       // rows in [N, Np) are written as zero codes
-      if (r0 + u * RPI < kRowsPerBlock && n < Np) *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
+      if (n < Np) *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
     }
   }
 }
