@@ -93,8 +93,8 @@ def sample_rows(N: int, tiles: int) -> np.ndarray:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path. "
-              "Per-head sharding would need no communication; see the design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path. "
+              "Sharding by head would need no communication between GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 
