@@ -57,24 +57,25 @@ int32_t err_chunks(int32_t BH, int64_t nrows) {
 }
 
 // exp2 patch table: binary32 patterns of x where v_exp_f32 would flip the
-// E4M3 code of S * 2^x (see the attention kernel).
-bool p_scale_setup(float S, bool* pow2, float* inv_S, uint32_t* bad0, uint32_t* bad1) {
+// E4M3 code of S * 2^x (see the attention kernel), and for each the adjacent
+// binary32 pattern whose v_exp_f32 result is the correctly rounded 2^x of the
+// listed x (both measured on gfx950 by running v_exp_f32 on every candidate).
+bool p_scale_setup(float S, bool* pow2, float* inv_S, uint32_t* bad0, uint32_t* bad1, uint32_t* rep0,
+                   uint32_t* rep1) {
   if (S == 448.0f) {
     *pow2 = false; *inv_S = 0.0f; *bad0 = 0xbf5a689au; *bad1 = 0xbfed344du;
+    *rep0 = 0xbf5a6899u; *rep1 = 0xbfed344cu;
     return true;
   }
   for (int k = 0; k <= 8; ++k) {
     if (S == ldexpf(1.0f, k)) {
       *pow2 = true; *inv_S = ldexpf(1.0f, -k); *bad0 = 0xbd3b9cb2u; *bad1 = 0xbef3efb2u;
+      *rep0 = 0xbd3b9cb1u; *rep1 = 0xbef3efb3u;
       return true;
     }
   }
   return false;
 }
-
-// 2^x rounded once to binary32 (the binary64 exp2 is accurate to well under
-// the distance of these 2^x from a binary32 rounding boundary).
-float rn32_exp2(float x) { return static_cast<float>(exp2(static_cast<double>(x))); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8A_OK : FP8A_ERR_HIP; }
 
@@ -178,7 +179,8 @@ int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const v
   bool pow2 = false;
   float inv_S = 0.0f;
   uint32_t bad0 = 0, bad1 = 0;
-  if (!p_scale_setup(p_scale, &pow2, &inv_S, &bad0, &bad1)) return FP8A_ERR_UNSUPPORTED;
+  uint32_t rep0 = 0, rep1 = 0;
+  if (!p_scale_setup(p_scale, &pow2, &inv_S, &bad0, &bad1, &rep0, &rep1)) return FP8A_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return FP8A_ERR_SHAPE;
   const float ls2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -207,8 +209,8 @@ int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const v
     memcpy(&x0, &bad0, 4);
     memcpy(&x1, &bad1, 4);
     p.xcheck = x0 < x1 ? x0 : x1;
-    p.fix0 = rn32_exp2(x0);
-    p.fix1 = rn32_exp2(x1);
+    p.rep0 = rep0;
+    p.rep1 = rep1;
   }
   const bool dump = p_dump != nullptr || row_hash != nullptr || row_zeros != nullptr;
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));

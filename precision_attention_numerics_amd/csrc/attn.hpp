@@ -25,7 +25,7 @@ struct FwdParams {
   float inv_S;            // 1/S when S is a power of two
   uint32_t bad0, bad1;    // binary32 patterns of x whose v_exp_f32 result would flip a code
   float xcheck;           // smaller of the two listed x: blocks whose largest x is below it need no fix-up
-  float fix0, fix1;       // RN32(2^x) for the two listed x
+  uint32_t rep0, rep1;    // neighbours of the listed x whose v_exp_f32 result is RN32(2^x) of the listed x
 };
 
 struct PcastParams {

@@ -190,9 +190,8 @@ __device__ __forceinline__ float column_sum(float v) {
 
 // P = 2^x for the tile's x (in place in s), sum of this lane's P into lpart,
 // E4M3 codes of S*P packed in the operand order of the P.V instruction.
-// FIX replaces the exp result for the two listed x by their correctly rounded
-// values (only run when a wave holds such an x).  MASK zeroes invisible keys.
-template <int T, bool MASK, bool FIX, bool CAUSAL, bool POW2, bool DUMP>
+// Invisible keys hold x = -inf (NaN when c = 0); MASK maps both to p = 0.
+template <int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T], float& lpart, uint32_t& zpart,
                                                                uint64_t& hpart, const int lim, const int i, const int jb,
                                                                const int N, const FwdParams& p,
@@ -206,14 +205,7 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float pv = __builtin_amdgcn_exp2f(x[t][r]);
-      if constexpr (FIX) {
-        const uint32_t xb = __float_as_uint(x[t][r]);
-        pv = (xb == p.bad0) ? p.fix0 : pv;
-        pv = (xb == p.bad1) ? p.fix1 : pv;
-      }
-      if constexpr (MASK) pv = (4 * t + r < lim) ? pv : 0.0f;
-      pr[r] = pv;
+      pr[r] = __builtin_amdgcn_exp2f(MASK ? __builtin_fmaxf(x[t][r], -INFINITY) : x[t][r]);
     }
     part[t] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
     // both halves of w are written below, so its initial bits are never
@@ -307,9 +299,10 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
   // for c > 0): the listed x can only occur in blocks holding keys near the
   // running max, and only there is each x screened.  (xb ^ B0) & (xb ^ B1) is
   // zero whenever xb is B0 or B1 (and for the few patterns that agree with B0
-  // or B1 bit by bit, which only cost a slower but still exact cast): one
-  // bit-op per x and a min over pairs, all in vector registers.  A wave
-  // holding a zero takes the cast that compares each x with the two patterns.
+  // or B1 bit by bit, which only cost the exact comparison below): one bit-op
+  // per x and a min over pairs, all in vector registers.  A wave holding a
+  // zero replaces each listed x by its neighbour pattern, whose v_exp_f32
+  // result is the correctly rounded 2^x of the listed x.
   bool fix = false;
   if (__any(__builtin_fmaf(bm, c, nmc) >= p.xcheck)) {
     uint32_t acc = 0xFFFFFFFFu;
@@ -322,14 +315,21 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
       }
     fix = __any(acc == 0u);
   }
+  if (__builtin_expect(fix, 0)) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t xb = __float_as_uint(s[t][r]);
+        xb = (xb == p.bad0) ? p.rep0 : xb;
+        xb = (xb == p.bad1) ? p.rep1 : xb;
+        s[t][r] = __uint_as_float(xb);
+      }
+  }
   float lpart;
   uint32_t zpart;
   uint64_t hpart;
-  v8i out;
-  if (__builtin_expect(fix, 0))
-    out = cast_tile<T, MASK, true, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
-  else
-    out = cast_tile<T, MASK, false, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
+  const v8i out = cast_tile<T, MASK, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
   hash += hpart;

@@ -1,7 +1,8 @@
 """GPU test of the exp fix-up: inputs built so that some key's exponent x equals
 exactly one of the binary32 values where the hardware exp2 would round the
 other way, in a masked (diagonal) and an unmasked block; every P code must
-still equal the oracle's (which uses the correctly rounded 2^x).
+still equal the oracle's (which uses the correctly rounded 2^x), and the
+timed variant (no dump) must return the dump variant's output bit for bit.
 
 Construction: Q rows are (448, 0, ..., 0) and K rows (a_j, 0, ..., 0) with a_j
 E4M3 values and max 448, so the codes are exact, both descales are 1 and each
@@ -67,8 +68,13 @@ def test_listed_x_values_cast_exactly(p_scale, which):
     gp = pipe.prepare(torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                       rotate=False, center=False)
     pd = torch.zeros((1, 1, N, N), dtype=torch.uint8, device="cuda")
-    pipe.fwd(gp, p_scale=p_scale, kv_order=1, block_n=128, causal=True, softmax_scale=scale, p_dump=pd)
+    kw = dict(p_scale=p_scale, kv_order=1, block_n=128, causal=True, softmax_scale=scale)
+    o_dump = pipe.fwd(gp, p_dump=pd, **kw)
+    # the timed variant (no dump; block 0 is unmasked for rows 128..255) takes
+    # the same fix-up and must give the same output bit for bit
+    o_timed = pipe.fwd(gp, **kw)
     torch.cuda.synchronize()
+    assert torch.equal(o_dump, o_timed), "timed and dump variants differ"
     op = oracle.prepare(q, k, v)
     assert op.q_desc.ravel()[0] == 1.0 and op.k_desc.ravel()[0] == 1.0
     ref = oracle.attention_fp8(op, p_scale=p_scale, kv_order=1, block_n=128, causal=True, softmax_scale=scale,
