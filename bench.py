@@ -182,12 +182,21 @@ def main():
         torch.cuda.synchronize()
         tb = time.perf_counter()
         prep_ms = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-        fwd_ms = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+        fwd_all = [e[1].elapsed_time(e[2]) for e in evs]
+        fwd_ms = np.mean(fwd_all)
         err_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
         o_rows = out[:, :, rows_dev.long()].cpu().numpy()
         rel_np = rel.cpu().numpy()
+        # prologue bytes: minimal = BF16 Q/K/V read once + one code byte
+        # written per element; two-pass = the max pass and the quantise pass
+        # each read Q/K/V (plus one more read of K for the mean when centred)
+        elems = B * (hq + 2 * hkv) * N * d
+        min_bytes = 3 * elems
+        two_pass = 5 * elems + (2 * B * hkv * N * d if synth.CONDITIONS[cond]["center"] else 0)
         res = {"ms_per_step": (tb - ta) * 1e3 / args.steps, "prepare_ms": float(prep_ms), "fwd_ms": float(fwd_ms),
-               "head_error_ms": float(err_ms)}
+               "fwd_median_ms": float(np.median(fwd_all)), "head_error_ms": float(err_ms),
+               "prepare_GBps_minimal_bytes": min_bytes / (prep_ms * 1e-3) / 1e9,
+               "prepare_GBps_two_pass_bytes": two_pass / (prep_ms * 1e-3) / 1e9}
         if ref_rows:
             lg = np.log1p(rel_np)
             res["log1p_rel_err_vs_f64"] = {"mean": float(lg.mean()), "max": float(lg.max()), "min": float(lg.min())}

@@ -90,6 +90,14 @@ def main(d: str):
             print(f"  MFMA busy fraction per SIMD: {g.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / simds / cyc:.3f}")
             print(f"  MFMA/VALU co-issue fraction: {g.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / simds / cyc:.3f}")
             print(f"  VALU instructions per MFMA: {g.get('SQ_INSTS_VALU', 0) / max(g.get('SQ_INSTS_MFMA', 1), 1):.2f}")
+            m_us = med.get(k)
+            if m_us:
+                # busy cycles per XCD over the same kernel's median duration in
+                # the trace run: the engine clock it ran at, and the dense FP8
+                # peak at that clock (256 CUs x 8192 FLOP per clock)
+                ghz = cyc / (m_us * 1e3)
+                print(f"  engine clock estimate (GRBM_GUI_ACTIVE / 8 / trace median): {ghz:.2f} GHz; "
+                      f"dense FP8 peak at that clock: {256 * 8192 * ghz / 1e3:.0f} TFLOP/s")
 
 
 def write_json(d: str, out: str):
