@@ -63,12 +63,12 @@ def copy_calibration(mib: int, steps: int):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4, "launches": steps}))
 
 
-def profiled_traffic(kernel: str):
+def profiled_traffic(kernel: str, summary: str = "attn_fwd_long_context_32k.json"):
     """HBM bytes per launch of the forward kernel from the committed rocprofv3
-    counters (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the kernel
-    source has changed since they were taken."""
+    counters (FETCH_SIZE + WRITE_SIZE, copy-scaled) in profiles/<summary>, or
+    None when the kernel source has changed since they were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attn_fwd_long_context_32k.json")
+    path = os.path.join(ROOT, "profiles", summary)
     src = os.path.join(ROOT, "precision_attention_numerics_amd", "csrc", "attn_fwd.hip")
     if not os.path.exists(path):
         return None
@@ -219,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3",
+        "dtype": "i8 (Q.K) + e4m3 (P.V)" if args.int8_qk else "e4m3",
         "data": "synthetic",
         "config": {"workload": "long-context causal FP8 attention forward, B=1, Hq=32, Hkv=8, d=128, N=%d, "
                                "BF16 sink-generator operands (Delta=8, 4 sinks), S=256, reverse KV order, block 128" % N,
@@ -229,8 +229,12 @@ def main():
                    "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": (None if (args.tile_scales or args.int8_qk) else
-                                 profiled_traffic("k_attn_fwd<128, 128, 2, true, true, false, false, false>")),
+                     "traffic": profiled_traffic(
+                         "k_attn_fwd<128, 128, 2, true, true, false, %s, %s>" % (
+                             "true" if args.tile_scales else "false", "true" if args.int8_qk else "false"),
+                         ("attn_fwd_tile_scaled_long_context_32k.json" if args.tile_scales else
+                          "attn_fwd_int8qk_long_context_32k.json" if args.int8_qk else
+                          "attn_fwd_long_context_32k.json")),
                      "kernel": "k_attn_fwd<128,128,2,causal,pow2%s%s>" % (",tiles" if args.tile_scales else "",
                                                                          ",int8qk" if args.int8_qk else ""),
                      "flop_per_launch": flop},
