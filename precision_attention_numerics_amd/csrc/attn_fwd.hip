@@ -59,8 +59,10 @@ __device__ __forceinline__ v4i lds_read16_i(const uint8_t* p) {
 // p = 2^x in binary32.  v_exp_f32 differs from the correctly rounded 2^x in
 // the last place for some x; exhaustive checks over every binary32 x in
 // [-150, 2^-8] show that for S = 2^k (k = 0..8) only two such x change an E4M3
-// code of S*p, and two other x for S = 448.  Those x are recomputed in
-// binary64 and rounded once.
+// code of S*p, and two other x for S = 448.  Here (the binary32 P-cast path)
+// those x are recomputed in binary64 and rounded once; the FP8 main loop
+// instead rewrites them to a neighbouring pattern whose v_exp_f32 result is
+// that correctly rounded value.
 __device__ __forceinline__ float exp2_code_exact(float x, uint32_t bad0, uint32_t bad1) {
   float p = __builtin_amdgcn_exp2f(x);
   const uint32_t xb = __float_as_uint(x);
