@@ -91,6 +91,33 @@ def test_reverse_S256_no_underflow_outside_sink_block(orc, sweep, delta):
     assert int(r.row_zeros.sum()) == 0
 
 
+@pytest.mark.parametrize("S", [1.0, 256.0])
+def test_codes_monotone_in_delta_and_reverse_order_isolation(orc, sweep, S):
+    """The sink generator draws the same numbers for every Delta and only adds
+    Delta*sqrt(d)*u to the four sink keys, so every non-sink logit is the same
+    at every Delta.  The running max that any block sees can only rise with
+    Delta, so every non-sink P~ code is non-increasing in Delta, in both
+    orders.  In reverse order the sinks' block (keys 0..127) is visited last,
+    so every earlier block sees exactly the same running max at every Delta
+    and its codes must not change at all."""
+    ref = {}
+    for delta in (0, 6, 12):
+        w = sweep[delta]
+        for order in (0, 1):
+            r = orc.attention_pcast_f32(w.q, w.k, w.v, p_scale=S, kv_order=order, block_n=128, causal=False,
+                                        rows=ROWS, want_p=True, k_sink=4)
+            ref[(delta, order)] = r.p[0, 0].astype(np.int64)
+    for order in (0, 1):
+        for lo, hi in ((0, 6), (6, 12)):
+            a, b = ref[(lo, order)][:, 4:], ref[(hi, order)][:, 4:]
+            assert np.all(a & 0x80 == 0) and np.all(b & 0x80 == 0)     # probabilities: non-negative codes
+            assert np.all(b <= a), (order, lo, hi, int((b > a).sum()))
+    assert np.array_equal(ref[(0, 1)][:, 128:], ref[(12, 1)][:, 128:])
+    # and the sinks' block does change (the test would be vacuous otherwise)
+    assert not np.array_equal(ref[(0, 1)][:, 4:128], ref[(12, 1)][:, 4:128])
+    assert not np.array_equal(ref[(0, 0)][:, 128:], ref[(12, 0)][:, 128:])
+
+
 def test_dp_sawtooth(orc):
     """Normalised maximum quantisation step of P under scale S: 2^-4 for every
     power of two, 14% higher for S = 448 (Optimalisatie 2, item 2), measured by
