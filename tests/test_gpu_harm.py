@@ -65,6 +65,9 @@ def test_rotation_harm_per_head(model):
         assert np.allclose(e, host, rtol=1e-9, atol=0), cond
         assert np.all(np.isfinite(e)) and np.all(e > 0)
 
+    print(f"[harm] {model} mean log1p(error vs binary64) per condition: "
+          + ", ".join(f"{c} {np.log1p(e).mean():.4f}" for c, e in errs.items()), flush=True)
+
     def harm(rot, unrot, e):
         lr = np.log1p(e[rot]).reshape(layers, texts, hq).mean(axis=1)
         lu = np.log1p(e[unrot]).reshape(layers, texts, hq).mean(axis=1)
