@@ -78,7 +78,8 @@ typedef struct {
   int64_t q_stride[3], k_stride[3], v_stride[3]; /* element strides of (batch, head, token) */
 } fp8a_shape;
 
-/* Np: the token count padded to a multiple of 128. */
+/* Np: the token count padded to a multiple of 128; 0 for a count outside
+ * [1, 2^30] (the range every entry point accepts). */
 int32_t fp8_attn_padded_seqlen(int32_t seqlen);
 
 /* Workspace needed by fp8_attn_prepare for this shape and flags (bytes). */

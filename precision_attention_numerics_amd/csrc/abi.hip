@@ -84,7 +84,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP8A_OK : FP8A_ERR_HIP; 
 extern "C" {
 
 int32_t fp8_attn_padded_seqlen(int32_t seqlen) {
-  if (seqlen < 1) return 0;
+  if (seqlen < 1 || seqlen > (1 << 30)) return 0;
   return (seqlen + 127) / 128 * 128;
 }
 

@@ -49,6 +49,8 @@ def test_no_torch_types_in_header():
 def test_pure_host_helpers(abi):
     assert abi.padded_seqlen(1) == 128 and abi.padded_seqlen(128) == 128 and abi.padded_seqlen(129) == 256
     assert abi.padded_seqlen(0) == 0
+    assert abi.padded_seqlen(1 << 30) == 1 << 30 and abi.padded_seqlen((1 << 30) + 1) == 0
+    assert abi.padded_seqlen(2**31 - 1) == 0
     for st in range(-6, 1):
         assert abi.strerror(st) != "unknown status"
     assert abi.strerror(-99) == "unknown status"
