@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["abi.hip", "prepare.hip", "attn_fwd.hip", "head_error.hip"]
+SOURCES = ["abi.hip", "prepare.hip", "attn_fwd.hip", "attn_fwd32.hip", "head_error.hip"]
 LIB = os.path.join(HERE, "libfp8attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

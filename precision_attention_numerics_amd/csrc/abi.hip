@@ -219,6 +219,7 @@ int fwd_common(const fp8a_shape* s, fp8a_dtype qkv_dtype, const void* q, const v
     p.rep1 = rep1;
   }
   const bool dump = p_dump != nullptr || row_hash != nullptr || row_zeros != nullptr;
+  if (s->head_dim == 64 && !p.int8) return hip_status(fp8a::launch_fwd_d64(p, block_n, causal != 0, pow2, dump, st));
   return hip_status(fp8a::launch_fwd(p, s->head_dim, block_n, causal != 0, pow2, dump, st));
 }
 

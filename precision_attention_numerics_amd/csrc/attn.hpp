@@ -43,6 +43,9 @@ struct PcastParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int D, int BC, bool causal, bool pow2, bool dump, hipStream_t st);
+// head_dim 64 with E4M3 Q/K on the 32x32x64 instruction (scores bit-identical
+// to the zero-padded 16x16x128 form)
+hipError_t launch_fwd_d64(const FwdParams& p, int BC, bool causal, bool pow2, bool dump, hipStream_t st);
 hipError_t launch_pcast_f32(const PcastParams& p, int D, bool pow2, hipStream_t st);
 
 struct HeadErrParams {
