@@ -66,14 +66,13 @@ def copy_calibration(mib: int, steps: int):
 def profiled_traffic(kernel: str, summary: str = "attn_fwd_long_context_32k.json"):
     """HBM bytes per launch of the forward kernel from the committed rocprofv3
     counters (FETCH_SIZE + WRITE_SIZE, copy-scaled) in profiles/<summary>, or
-    None when the kernel source has changed since they were taken."""
-    import hashlib
+    None when the kernel sources have changed since they were taken."""
+    from precision_attention_numerics_amd.profile_summary import kernel_source_sha256
     path = os.path.join(ROOT, "profiles", summary)
-    src = os.path.join(ROOT, "precision_attention_numerics_amd", "csrc", "attn_fwd.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     for name, v in rec["kernels"].items():
         if name.startswith(kernel):

@@ -100,8 +100,22 @@ def main(d: str):
                       f"dense FP8 peak at that clock: {256 * 8192 * ghz / 1e3:.0f} TFLOP/s")
 
 
-def write_json(d: str, out: str):
+# every source the forward kernels are compiled from: counters recorded for
+# one version are not used for another
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_fwd32.hip", "attn_common.hpp", "attn.hpp", "device_common.hpp")
+
+
+def kernel_source_sha256() -> str:
     import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def write_json(d: str, out: str):
     import json
     fetch = counters(os.path.join(d, "fetch", "fetch_counter_collection.csv"))
     write = counters(os.path.join(d, "write", "write_counter_collection.csv"))
@@ -109,8 +123,7 @@ def write_json(d: str, out: str):
     copyw = counters(os.path.join(d, "copyw", "copyw_counter_collection.csv"))
     f_scale = COPY_BYTES / (max(v for (k, c), v in copyf.items() if "elementwise" in k) * 1024)
     w_scale = COPY_BYTES / (max(v for (k, c), v in copyw.items() if "elementwise" in k) * 1024)
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "attn_fwd.hip")
-    res = {"kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(), "kernels": {}}
+    res = {"kernel_source_sha256": kernel_source_sha256(), "kernels": {}}
     for (k, c), v in fetch.items():
         if "k_attn_fwd" in k:
             res["kernels"].setdefault(k, {})["read_bytes"] = v * 1024 * f_scale
