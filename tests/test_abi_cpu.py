@@ -164,3 +164,26 @@ def test_head_error_rejects(abi):
     assert f(ctypes.byref(ok), FAKE, FAKE, 1, None, 64, FAKE, FAKE, 1 << 20, None) == -3   # bf16 reference
     assert f(ctypes.byref(ok), None, FAKE, 0, None, 64, FAKE, FAKE, 1 << 20, None) == -1
     assert f(ctypes.byref(ok), FAKE, FAKE, 0, None, 64, FAKE, None, 0, None) == -5
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """include/fp8_attn.h compiles as strict C99 and a C program links against
+    the library and calls its host-side functions (no C++ or torch needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "fp8_attn.h"\n'
+        "int main(void) {\n"
+        "  fp8a_shape s = {1, 2, 1, 64, 64, {0, 0, 0}, {0, 0, 0}, {0, 0, 0}};\n"
+        '  printf("%d %d\\n", fp8_attn_padded_seqlen(s.seqlen), (int)fp8_attn_prepare_workspace_bytes(&s, FP8A_ROTATE_QK) > 0);\n'
+        "  return 0;\n}\n")
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(LIB)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER),
+                    str(src), "-L", libdir, "-lfp8attn", "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out == ["128", "1"]
