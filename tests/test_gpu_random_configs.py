@@ -2,7 +2,7 @@
 query/KV heads (GQA ratios 1-7), ragged sequence length, head_dim, KV block,
 order, static scale S, causal or not, prologue condition and scale/code
 variant (per head, per 128-token tile with or without prefix maxima, int8
-Q/K).  Each case must meet the same bar as the fixed cases: prologue codes and
+Q/K) and input storage (dense, token-major, padded token stride).  Each case must meet the same bar as the fixed cases: prologue codes and
 descales bit-exact, every P~ code, underflow count and row checksum equal to
 the oracle's, the timed variant's output equal to the dump variant's bit for
 bit, and the output within 2e-3 per head of the oracle's emulated result.
@@ -34,9 +34,24 @@ def draw(i: int) -> dict:
     cond = str(g.choice(list(synth.CONDITIONS)))
     variant = str(g.choice(["head", "head", "head", "tiles", "int8"]))
     prefix = variant == "tiles" and not synth.CONDITIONS[cond]["center"] and bool(g.integers(2))
-    return dict(d=d, hkv=hkv, hq=hkv * group, B=B, N=N, cond=cond, variant=variant, prefix=prefix,
-                block_n=int(g.choice([64, 128])), kv_order=int(g.integers(2)),
-                p_scale=float(g.choice([1.0, 2.0, 16.0, 256.0, 448.0])), causal=bool(g.integers(2)))
+    c = dict(d=d, hkv=hkv, hq=hkv * group, B=B, N=N, cond=cond, variant=variant, prefix=prefix,
+             block_n=int(g.choice([64, 128])), kv_order=int(g.integers(2)),
+             p_scale=float(g.choice([1.0, 2.0, 16.0, 256.0, 448.0])), causal=bool(g.integers(2)))
+    # input storage: dense [B,H,N,d], [B,N,H,d] storage seen as [B,H,N,d], or
+    # a token stride padded to d + 64 elements
+    c["layout"] = str(g.choice(["dense", "dense", "bnhd", "padded"]))
+    return c
+
+
+def device_input(x: np.ndarray, dtype: str, layout: str) -> torch.Tensor:
+    t = dev(x, dtype)
+    if layout == "bnhd":
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+    if layout == "padded":
+        buf = torch.zeros(t.shape[:-1] + (t.shape[-1] + 64,), dtype=t.dtype, device=t.device)
+        buf[..., :t.shape[-1]] = t
+        return buf[..., :t.shape[-1]]
+    return t
 
 
 def workload(i: int, c: dict) -> synth.Workload:
@@ -66,7 +81,9 @@ def test_random_config(i):
     extra = dict(tiles=c["variant"] == "tiles", prefix=c["prefix"], int8=c["variant"] == "int8")
     print(f"random case {i}: {c}", flush=True)
     pipe = pan.AttnPipeline(B, hq, hkv, N, d)
-    gp = pipe.prepare(dev(w.q, w.dtype), dev(w.k, w.dtype), dev(w.v, w.dtype), signs=signs_dev(w), **flags, **extra)
+    lay = c["layout"]
+    gp = pipe.prepare(device_input(w.q, w.dtype, lay), device_input(w.k, w.dtype, lay),
+                      device_input(w.v, w.dtype, lay), signs=signs_dev(w), **flags, **extra)
     op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, **flags, **extra)
     torch.cuda.synchronize()
     compare_prepared(gp, op, N, flags["center"])
