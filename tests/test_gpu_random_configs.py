@@ -103,3 +103,34 @@ def test_random_config(i):
     assert np.array_equal(rz.cpu().numpy().astype(np.uint32), ref.row_zeros), "underflow counts differ"
     assert np.array_equal(rh.cpu().numpy().view(np.uint64), oracle.row_hash(ref.p)), "row checksums differ"
     assert max_head_rel(o, ref.out) <= TOL_O
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("i", range(40))
+def test_random_pcast_config(i):
+    """The binary32 P-cast-only path (only P cast to E4M3) on random shapes:
+    every P~ code, underflow count and row checksum equal to the oracle's,
+    output within 2e-3 per head."""
+    import precision_attention_numerics_amd as pan
+    c = draw(1000 + i)
+    w = workload(1000 + i, c)
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float32) for x in (w.q, w.k, w.v))
+    B, hq, N, d = q.shape
+    hkv = k.shape[1]
+    print(f"random P-cast case {i}: {dict((x, c[x]) for x in ('B', 'hq', 'hkv', 'N', 'd', 'block_n', 'kv_order', 'p_scale', 'causal'))}",
+          flush=True)
+    pipe = pan.AttnPipeline(B, hq, hkv, N, d)
+    kw = dict(p_scale=c["p_scale"], kv_order=c["kv_order"], block_n=c["block_n"], causal=c["causal"])
+    pd = torch.zeros((B, hq, N, N), dtype=torch.uint8, device="cuda")
+    rz = torch.zeros((B, hq, N), dtype=torch.int32, device="cuda")
+    rh = torch.zeros((B, hq, N), dtype=torch.int64, device="cuda")
+    out = pipe.fwd_f32(dev(q, "f32"), dev(k, "f32"), dev(v, "f32"), p_dump=pd, row_hash=rh, row_zeros=rz, k_sink=4,
+                       **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_pcast_f32(q, k, v, want_p=True, k_sink=4, **kw)
+    P = pd.cpu().numpy()
+    nbad = p_mismatch(P, ref.p)
+    assert nbad == 0, f"{nbad} P codes differ, first at {np.argwhere(P != ref.p)[:5]}"
+    assert np.array_equal(rz.cpu().numpy().astype(np.uint32), ref.row_zeros), "underflow counts differ"
+    assert np.array_equal(rh.cpu().numpy().view(np.uint64), oracle.row_hash(ref.p)), "row checksums differ"
+    assert max_head_rel(out.cpu().numpy(), ref.out) <= TOL_O
