@@ -146,7 +146,7 @@ __device__ __forceinline__ float column_sum(float v) {
 // Invisible keys hold x = -inf (NaN when c = 0); MASK maps both to p = 0.
 template <int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T], float& lpart, uint32_t& zpart,
-                                                               uint64_t& hpart, const int lim, const int i, const int jb,
+                                                               uint64_t& hpart, const int i, const int jb,
                                                                const int N, const FwdParams& p,
                                                                uint8_t* __restrict__ dump_row) {
   v8i out;
@@ -282,7 +282,7 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
   float lpart;
   uint32_t zpart;
   uint64_t hpart;
-  const v8i out = cast_tile<T, MASK, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
+  const v8i out = cast_tile<T, MASK, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
   hash += hpart;

@@ -121,7 +121,7 @@ __device__ __forceinline__ void fill_v(const __amdgpu_buffer_rsrc_t vrs, int blk
 // MASK maps both to p = 0.
 template <int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
 __device__ __attribute__((always_inline)) inline void cast32(const v16f (&x)[T], v8i (&pop)[T / 2], float& lpart,
-                                                             uint32_t& zpart, uint64_t& hpart, const int lim, const int i,
+                                                             uint32_t& zpart, uint64_t& hpart, const int i,
                                                              const int jb, const int N, const FwdParams& p,
                                                              uint8_t* __restrict__ dump_row) {
   float part[T * 4];
@@ -256,7 +256,7 @@ __device__ __attribute__((always_inline)) inline void softmax32(v16f (&s)[T], v8
   float lpart;
   uint32_t zpart;
   uint64_t hpart;
-  cast32<T, MASK, CAUSAL, POW2, DUMP>(s, pop, lpart, zpart, hpart, lim, i, jb, N, p, dump_row);
+  cast32<T, MASK, CAUSAL, POW2, DUMP>(s, pop, lpart, zpart, hpart, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
   hash += hpart;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kErrThreads) void k_head_err_partial(const HeadErrP
   sd[threadIdx.x] = den;
   __syncthreads();
   for (int w = kErrThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
+    if (static_cast<int>(threadIdx.x) < w) {
       sn[threadIdx.x] += sn[threadIdx.x + w];
       sd[threadIdx.x] += sd[threadIdx.x + w];
     }
