@@ -370,6 +370,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd32(const FwdParams p) {
   // block it-1 (buffer (it-1)&1), and fills K of block it+1 (buffer (it+1)&1)
   // and V of block it (buffer it&1) -- in both cases the buffer whose last
   // reader was iteration it-1, which every wave has left at the barrier.
+  // Iteration 0 multiplies the zero codes in pprev with V^T buffer 1, which is
+  // cleared here so that the product is exactly zero.
   fill_k<D, BC>(krs, p.kv_order ? jmax : 0, wv, koff, klds);
 #pragma unroll
   for (int u = tid; u < KBYTES / 16; u += kThreads) *reinterpret_cast<u32x4*>(vlds + KBYTES + 16 * u) = u32x4{0, 0, 0, 0};

@@ -101,8 +101,16 @@ def main(d: str):
 
 
 # every source the forward kernels are compiled from: counters recorded for
-# one version are not used for another
+# one version of the code are not used for another (comments and layout do
+# not count: they are removed before hashing)
 KERNEL_SOURCES = ("attn_fwd.hip", "attn_fwd32.hip", "attn_common.hpp", "attn.hpp", "device_common.hpp")
+
+
+def _code_only(text: str) -> str:
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_source_sha256() -> str:
@@ -111,7 +119,7 @@ def kernel_source_sha256() -> str:
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
     for name in KERNEL_SOURCES:
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, name)).read()).encode())
     return h.hexdigest()
 
 
