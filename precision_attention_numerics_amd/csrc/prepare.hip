@@ -330,19 +330,23 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
   const float qmax = int8 ? 127.0f : 448.0f;
   constexpr int L = D / 8;
   constexpr int RPI = kPrepThreads / L;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  // Blocks take heads and row ranges in the reverse of the max pass's order:
+  // the rows that pass read last are the likeliest still to sit in the
+  // memory-side cache, and they are read first here.
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int bh = gridDim.y - 1 - blockIdx.y, b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
   const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
-  const int n_begin = blockIdx.x * kRowsPerBlock;
+  const int n_begin = bx * kRowsPerBlock;
   // scales of the block's rows [0, 128) and [128, 256)
   float inv, desc, inv_hi, desc_hi;
   if (ntile == 1) {
     scales_from_amax(amax[bh], ROT, cd, inv, desc, qmax);
     inv_hi = inv;
     desc_hi = desc;
-    if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+    if (bx == 0 && threadIdx.x == 0) desc_out[bh] = desc;
   } else {
-    const int64_t t0 = static_cast<int64_t>(bh) * ntile + 2 * blockIdx.x;
+    const int64_t t0 = static_cast<int64_t>(bh) * ntile + 2 * bx;
     const bool has_hi = n_begin + kRowsPerBlock / 2 < Np;   // the block's second tile exists
     scales_from_amax(amax[t0], ROT, cd, inv, desc, qmax);
     scales_from_amax(has_hi ? amax[t0 + 1] : 0u, ROT, cd, inv_hi, desc_hi, qmax);
@@ -401,13 +405,15 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_vt(const IT* __restrict_
   constexpr int TOK = 128;
   constexpr int LDSW = TOK + 16;           // padded row of the channel-major tile
   __shared__ __align__(16) uint8_t tile[D * LDSW];
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  // reverse of the max pass's order, as in k_quant_rows
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int bh = gridDim.y - 1 - blockIdx.y, b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
   float inv, desc;
   scales_from_amax(amax[bh], false, 1.0f, inv, desc);
-  if (blockIdx.x == 0 && threadIdx.x == 0) desc_out[bh] = desc;
+  if (bx == 0 && threadIdx.x == 0) desc_out[bh] = desc;
   const IT* base = v + b * sb + h * sh + 8 * li;
-  const int n0 = blockIdx.x * TOK;
+  const int n0 = bx * TOK;
   for (int r = rl; r < TOK; r += RPI) {
     const int n = n0 + r;
     uint32_t lo = 0, hi = 0;
@@ -451,48 +457,50 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   uint32_t* amax_q = a.amax;
   uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq * nt;
   uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv * nt;
+  const dim3 gq((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
+  const dim3 gk((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
+  const dim3 gq_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
+  const dim3 gk_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
+  const float* mu = a.k_mean;
+  const int i8 = a.int8 ? 1 : 0;
+  // Each tensor's passes run back to back (max, then quantise), so the
+  // quantise pass finds the rows the max pass read last still cached.
+  if (a.rotate) {
+    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, nt, amax_q, a.status);
+    if (a.prefix) k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
+    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, i8, a.q_desc, a.q8);
+  } else {
+    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, nt, amax_q, a.status);
+    if (a.prefix) k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
+    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, i8, a.q_desc, a.q8);
+  }
   if (a.center) {
     constexpr int32_t kChunksPerBlock = 256 / (D / 8);
     k_kmean_partial<IT, D><<<dim3((a.np2 + kChunksPerBlock - 1) / kChunksPerBlock, B * hkv), dim3(256), 0, st>>>(
         k, a.ks[0], a.ks[1], a.ks[2], hkv, N, a.np2, a.mean_part);
     k_kmean_final<<<dim3(B * hkv, D / kMeanCh), dim3(kMeanCh * kMeanW), 0, st>>>(a.mean_part, a.np2, N, D, a.k_mean);
   }
-  const dim3 gq((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
-  const dim3 gk((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
-  const dim3 gq_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
-  const dim3 gk_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
-  const float* mu = a.k_mean;
-  if (a.rotate) {
-    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, nt, amax_q, a.status);
-    if (a.center)
-      k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, a.signs, nt, amax_k, a.status);
-    else
-      k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, a.signs, nt, amax_k, a.status);
+  const int8_t* ks = a.rotate ? a.signs : nullptr;
+  if (a.rotate && a.center) {
+    k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, ks, nt, amax_k, a.status);
+  } else if (a.rotate) {
+    k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, ks, nt, amax_k, a.status);
+  } else if (a.center) {
+    k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, nt, amax_k, a.status);
   } else {
-    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, nt, amax_q, a.status);
-    if (a.center)
-      k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, nt, amax_k, a.status);
-    else
-      k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, nt, amax_k, a.status);
+    k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, nt, amax_k, a.status);
+  }
+  if (a.prefix) k_prefix_max<<<dim3((B * hkv + 255) / 256), blk, 0, st>>>(amax_k, B * hkv, nt);
+  if (a.rotate && a.center) {
+    k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, ks, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+  } else if (a.rotate) {
+    k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, ks, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+  } else if (a.center) {
+    k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+  } else {
+    k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
   }
   k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, 1, amax_v, a.status);
-  if (a.prefix) {
-    k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
-    k_prefix_max<<<dim3((B * hkv + 255) / 256), blk, 0, st>>>(amax_k, B * hkv, nt);
-  }
-  if (a.rotate) {
-    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, a.int8 ? 1 : 0, a.q_desc, a.q8);
-    if (a.center)
-      k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, a.signs, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
-    else
-      k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, a.signs, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
-  } else {
-    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, a.int8 ? 1 : 0, a.q_desc, a.q8);
-    if (a.center)
-      k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
-    else
-      k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, a.int8 ? 1 : 0, a.k_desc, a.k8);
-  }
   k_quant_vt<IT, D><<<dim3(Np / 128, B * hkv), blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, Np, amax_v, a.v_desc, a.v8t);
   (void)grp;
   return hipGetLastError();
