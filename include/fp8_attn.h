@@ -146,8 +146,8 @@ int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
  *              FP8A_I8QK: the same with int8 q and k codes (an INT8_QK
  *              prologue); the score is their exact integer dot product.
  *              FP8A_F32: dense binary32 q/k/v [B,h,N,d], only P is cast
- *              ("kernel-faithful" simulation of the P-Cast summary, Bijdragen
- *              item 4); scores are an ordered binary32 fma chain over the
+ *              (the P-Cast summary's simulation that follows the kernel step
+ *              by step, Bijdragen item 4); scores are an ordered binary32 fma chain over the
  *              channels; descales must be NULL.
  *   softmax_scale  > 0, usually 1/sqrt(d).
  *   p_scale    S: a power of two in [1, 256] or 448.
@@ -200,8 +200,8 @@ size_t fp8_attn_head_error_workspace_bytes(const fp8a_shape* shape, int64_t nrow
 /*
  * fp8_attn_head_error -- relative Frobenius output error per (batch, head):
  * rel_err[b*hq+h] = ||O - R||_F / ||R||_F over the head's rows, sums in
- * binary64 (project page: each head's output against ideal causal FP64
- * attention; study page, "What do these scores mean?").
+ * binary64 (project page: each head's output against exact causal attention
+ * in binary64; study page, "What do these scores mean?").
  *
  *   out        device, float [B,hq,N,d] (as written by fp8_attn_fwd).
  *   ref        device, [B,hq,nrows,d] of ref_dtype FP8A_F32 or FP8A_F64.

@@ -8,8 +8,8 @@ code with them.
 What it computes (each function cites the passage it follows):
 
 * :func:`attention_f64` -- ideal attention in binary64, the reference every
-  head is measured against ("ideal causal FP64 attention", attention-numerics
-  project page, first section).
+  head is measured against (attention-numerics project page, first section:
+  each head's output is compared with exact causal attention in binary64).
 * :func:`prepare` -- the quantisation prologue: per-(batch, head) max scales
   over the full sequence, optional mean-key centring before an optional
   random-sign Hadamard rotation of Q and K (never V), E4M3FN codes with
@@ -291,8 +291,8 @@ def attention_pcast_f32(q, k, v, softmax_scale: float | None = None, p_scale: fl
                         kv_order: int = 0, block_n: int = 128, causal: bool = False, rows=None,
                         want_p: bool = False, k_sink: int = 0, p_cast: bool = True,
                         nthreads: int | None = None) -> LoopResult:
-    """Main loop with binary32 Q/K/V, only P cast ("kernel-faithful" simulation,
-    P-Cast summary, Bijdragen item 4).  p_cast=False keeps P in binary32."""
+    """Main loop with binary32 Q/K/V, only P cast (the P-Cast summary's
+    simulation that follows the kernel step by step, Bijdragen item 4).  p_cast=False keeps P in binary32."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
     v = np.ascontiguousarray(v, dtype=np.float32)

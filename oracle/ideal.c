@@ -1,7 +1,7 @@
 /*
  * Ideal attention in binary64 -- the reference every head's output is
- * compared against ("ideal causal FP64 attention", attention-numerics project
- * page, first section).  TEST INFRASTRUCTURE ONLY (see oracle.h).
+ * compared against (attention-numerics project page, first section: exact
+ * causal attention computed in binary64).  TEST INFRASTRUCTURE ONLY (see oracle.h).
  *
  * Plain definition: for query i, logits z_j = (q_i . k_j) * scale over the
  * visible keys (j <= i when causal, every key otherwise), weights

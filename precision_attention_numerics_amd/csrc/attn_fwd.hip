@@ -505,8 +505,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 }
 
 // -------------------------------------------------------- P-cast-only path
-// Binary32 Q/K/V, only P cast (the "kernel-faithful" simulation of the P-Cast
-// summary, Bijdragen item 4).  One thread per query row; the score is an
+// Binary32 Q/K/V, only P cast (the P-Cast summary's simulation that follows
+// the kernel step by step, Bijdragen item 4).  One thread per query row; the score is an
 // ordered binary32 fma chain over the channels.  Not a throughput path.
 template <int D, bool POW2>
 __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {

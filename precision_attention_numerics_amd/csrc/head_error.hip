@@ -1,6 +1,6 @@
 // Relative Frobenius output error per (batch, head) for gfx950: the per-head
 // metric of the attention-numerics pages (project page: each head's output
-// against ideal causal FP64 attention; study page, "What do these scores
+// against exact causal attention in binary64; study page, "What do these scores
 // mean?": log(1 + relative Frobenius error) per text).  The log and the mean
 // over texts are taken by the caller on the B*hq values returned here.
 //
