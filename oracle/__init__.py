@@ -24,9 +24,12 @@ What it computes (each function cites the passage it follows):
   unrotated (study page, "What do these scores mean?").
 
 Every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, invariants, brute force or printed values; the one
-documented exception (the shared-key illustration, whose vectors the page does
-not print) is marked "parity unpinned" there.
+against closed forms, invariants, brute force or printed values.  Parity
+unpinned against the pages: the shared-key illustration, whose vectors the
+page does not print, and the matrix-unit score model of :func:`fp8_dot128`
+(``mode="mfma"``), which the pages do not describe; it is held by invariants
+(the exact sum when nothing is truncated, symmetry in its operands, an error
+bound), not by a printed value.
 """
 from __future__ import annotations
 
