@@ -216,6 +216,12 @@ int fp8_attn_head_error(const fp8a_shape* shape, const float* out, const void* r
 /* Static description of a status code. */
 const char* fp8_attn_strerror(int status);
 
+/* Static string identifying the build: "source_sha256=<hex> arch=gfx950",
+ * the SHA-256 the build script computed over the library's sources, headers
+ * and itself, so a caller can check that a shipped binary matches a source
+ * tree.  Not part of the computation; never fails. */
+const char* fp8_attn_build_info(void);
+
 #ifdef __cplusplus
 }
 #endif

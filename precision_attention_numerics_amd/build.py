@@ -1,4 +1,11 @@
-"""Builds the HIP library libfp8attn.so for gfx950 (in-tree, next to this file)."""
+"""Builds the HIP library libfp8attn.so for gfx950 (in-tree, next to this file).
+
+Each source is compiled to an object in parallel, then the objects are linked.
+This module is importable without the package (it imports nothing from it), so
+a fresh checkout can build before the library exists.
+"""
+import concurrent.futures
+import hashlib
 import os
 import subprocess
 import sys
@@ -8,31 +15,74 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["abi.hip", "prepare.hip", "attn_fwd.hip", "attn_fwd32.hip", "head_error.hip"]
 LIB = os.path.join(HERE, "libfp8attn.so")
+OBJDIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMPILE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # every binary32 operation on the P path is an explicit single operation
     "-ffp-contract=off",
     # no packed FP32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
-    # a symbol left undefined (e.g. a kernel launch stub the host pass did not
-    # emit) fails the build instead of the first load
-    "-Wl,--no-undefined",
 ]
+# a symbol left undefined (e.g. a kernel launch stub the host pass did not
+# emit) fails the build instead of the first load
+LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined"]
+
+
+def source_files() -> list[str]:
+    """Every file the library is built from (sources, headers, this script)."""
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".hpp"))]
+    files.append(os.path.join(ROOT, "include", "fp8_attn.h"))
+    files.append(os.path.abspath(__file__))
+    return files
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _filter(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines()
+                     if "packed-fp32-ops" not in l and "unknown target feature" not in l)
+
+
+def _compile(src: str, obj: str, extra: list[str]) -> tuple[str, int, str]:
+    cmd = [HIPCC] + COMPILE_FLAGS + extra + ["-c", "-o", obj, src]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return " ".join(cmd), res.returncode, _filter(res.stderr)
 
 
 def build(verbose: bool = False) -> str:
-    cmd = [HIPCC] + FLAGS + ["-o", LIB + ".tmp"] + [os.path.join(CSRC, s) for s in SOURCES]
+    os.makedirs(OBJDIR, exist_ok=True)
+    digest = source_hash()
+    # the library reports the hash of the sources it was built from
+    extra = [f"-DFP8A_SOURCE_SHA256=\"{digest}\""]
+    jobs = []
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        for s in SOURCES:
+            obj = os.path.join(OBJDIR, s.replace(".hip", ".o"))
+            jobs.append(ex.submit(_compile, os.path.join(CSRC, s), obj, extra))
+        for j in jobs:
+            cmd, rc, err = j.result()
+            if verbose:
+                print(cmd, flush=True)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}):\n{cmd}\n{err}")
+            if verbose and err.strip():
+                print(err)
+    objs = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES]
+    cmd = [HIPCC] + LINK_FLAGS + ["-o", LIB + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and "unknown target feature" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_filter(res.stderr)}")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -270,6 +270,14 @@ int fp8_attn_head_error(const fp8a_shape* s, const float* out, const void* ref, 
   return hip_status(fp8a::launch_head_error(p, static_cast<hipStream_t>(stream)));
 }
 
+#ifndef FP8A_SOURCE_SHA256
+#define FP8A_SOURCE_SHA256 "unknown"
+#endif
+
+const char* fp8_attn_build_info(void) {
+  return "source_sha256=" FP8A_SOURCE_SHA256 " arch=gfx950";
+}
+
 const char* fp8_attn_strerror(int status) {
   switch (status) {
     case FP8A_OK: return "ok";

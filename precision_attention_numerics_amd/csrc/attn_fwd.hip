@@ -19,6 +19,8 @@
 //    never goes through LDS.
 //  * Workgroups are ordered longest-first (causal) and grouped by head per XCD
 //    so the K/V of a head stay in one XCD's L2.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn.hpp"
 
@@ -197,15 +199,15 @@ __device__ __attribute__((always_inline)) inline v8i cast_tile(const v4f (&x)[T]
   return out;
 }
 
-// Online-softmax update of one 16-row query tile for one block and the P
-// cast.  The lane holds query i and keys jb + 4t + r (t < T, r < 4); s holds
-// the scores on entry and x = s*c - RN32(m*c) on exit.
-template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP, bool TILES>
-__device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], const float c, float& ms, float& mcp,
-                                                                  float& lsum, v4f (&oacc)[D / 16], const int i,
-                                                                  const int jb, const int N, const FwdParams& p,
-                                                                  uint32_t& zeros, uint64_t& hash,
-                                                                  uint8_t* __restrict__ dump_row) {
+// Online-softmax update of one 16-row query tile for one block, first part:
+// masking, block max, running max, alpha, l and O rescaled, and s replaced by
+// x = fma(s, c, -RN32(m*c)).  The lane holds query i and keys jb + 4t + r
+// (t < T, r < 4).  Returns the wave-uniform decision whether some x of the
+// tile can be one of the listed exponents (softmax_screen).
+template <int D, int T, bool MASK, bool CAUSAL, bool TILES>
+__device__ __attribute__((always_inline)) inline bool softmax_front(v4f (&s)[T], const float c, float& ms, float& mcp,
+                                                                    float& lsum, v4f (&oacc)[D / 16], const int i,
+                                                                    const int jb, const int N, const FwdParams& p) {
   // key jb + k is visible iff k < lim (k = 4t + r): one compare per key
   const int lim = min(N, CAUSAL ? i + 1 : N) - jb;
   if constexpr (MASK) {
@@ -250,25 +252,27 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
     for (int r = 0; r < 4; ++r) s[t][r] = __builtin_fmaf(s[t][r], c, nmc);
   // Every x of this row is at most fma(bm, c, -mc) (the fma is monotone in s
   // for c > 0): the listed x can only occur in blocks holding keys near the
-  // running max, and only there is each x screened.  (xb ^ B0) & (xb ^ B1) is
-  // zero whenever xb is B0 or B1 (and for the few patterns that agree with B0
-  // or B1 bit by bit, which only cost the exact comparison below): one bit-op
-  // per x and a min over pairs, all in vector registers.  A wave holding a
-  // zero replaces each listed x by its neighbour pattern, whose v_exp_f32
-  // result is the correctly rounded 2^x of the listed x.
-  bool fix = false;
-  if (__any(__builtin_fmaf(bm, c, nmc) >= p.xcheck)) {
-    uint32_t acc = 0xFFFFFFFFu;
+  // running max, and only there is each x screened.
+  return __any(__builtin_fmaf(bm, c, nmc) >= p.xcheck);
+}
+
+// The exp screen of one tile's x: (xb ^ B0) & (xb ^ B1) is zero whenever xb
+// is B0 or B1 (and for the few patterns that agree with B0 or B1 bit by bit,
+// which only cost the exact comparison below): one bit-op per x and a min
+// over pairs, all in vector registers.  A wave holding a zero replaces each
+// listed x by its neighbour pattern, whose v_exp_f32 result is the correctly
+// rounded 2^x of the listed x.
+template <int T>
+__device__ __attribute__((always_inline)) inline void softmax_screen(v4f (&s)[T], const FwdParams& p) {
+  uint32_t acc = 0xFFFFFFFFu;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+  for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t xb = __float_as_uint(s[t][r]);
-        acc = min(acc, (xb ^ p.bad0) & (xb ^ p.bad1));
-      }
-    fix = __any(acc == 0u);
-  }
-  if (__builtin_expect(fix, 0)) {
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t xb = __float_as_uint(s[t][r]);
+      acc = min(acc, (xb ^ p.bad0) & (xb ^ p.bad1));
+    }
+  if (__builtin_expect(__any(acc == 0u), 0)) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -279,14 +283,36 @@ __device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], c
         s[t][r] = __uint_as_float(xb);
       }
   }
+}
+
+// Last part: p = 2^x, l += sum p, and the E4M3 codes of S*p as the B operand
+// of the P.V instruction.
+template <int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP>
+__device__ __attribute__((always_inline)) inline v8i softmax_back(const v4f (&x)[T], float& lsum, const int i,
+                                                                  const int jb, const int N, const FwdParams& p,
+                                                                  uint32_t& zeros, uint64_t& hash,
+                                                                  uint8_t* __restrict__ dump_row) {
   float lpart;
   uint32_t zpart;
   uint64_t hpart;
-  const v8i out = cast_tile<T, MASK, CAUSAL, POW2, DUMP>(s, lpart, zpart, hpart, i, jb, N, p, dump_row);
+  const v8i out = cast_tile<T, MASK, CAUSAL, POW2, DUMP>(x, lpart, zpart, hpart, i, jb, N, p, dump_row);
   lsum = lsum + lpart;
   zeros += zpart;
   hash += hpart;
   return out;
+}
+
+// Online-softmax update of one 16-row query tile for one block and the P
+// cast (the three parts above in order); s holds the scores on entry and x on
+// exit.
+template <int D, int T, bool MASK, bool CAUSAL, bool POW2, bool DUMP, bool TILES>
+__device__ __attribute__((always_inline)) inline v8i softmax_tile(v4f (&s)[T], const float c, float& ms, float& mcp,
+                                                                  float& lsum, v4f (&oacc)[D / 16], const int i,
+                                                                  const int jb, const int N, const FwdParams& p,
+                                                                  uint32_t& zeros, uint64_t& hash,
+                                                                  uint8_t* __restrict__ dump_row) {
+  if (softmax_front<D, T, MASK, CAUSAL, TILES>(s, c, ms, mcp, lsum, oacc, i, jb, N, p)) softmax_screen<T>(s, p);
+  return softmax_back<T, MASK, CAUSAL, POW2, DUMP>(s, lsum, i, jb, N, p, zeros, hash, dump_row);
 }
 
 template <int D, int BC, int QT, bool CAUSAL, bool POW2, bool DUMP, bool TILES, bool I8>
@@ -504,6 +530,471 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
   }
 }
 
+// ------------------------------------------------ software-pipelined loop
+// The same computation as k_attn_fwd for head_dim 128, KV blocks of 128 keys,
+// E4M3 scores and no per-key outputs (P dump, checksums, underflow counts).
+// Each query tile goes through the same operations on the same values in the
+// same order as there, so the outputs are bit-identical; only the issue order
+// changes.  The loop is pipelined across blocks: step n issues
+//   run 1: Q.K^T of block n+1 for both 16-row tiles (one LDS read of each K
+//          tile serves both), each pair of matrix instructions followed by the
+//          exp / row-sum / E4M3-cast work of block n on the same key tile
+//          (the scores' registers are consumed as the new scores arrive);
+//   run 2: P.V of block n for both tiles (one LDS read of each V^T tile),
+//          each O tile rescaled by block n's alpha just before its matrix
+//          instruction, followed by the max / fma work of block n+1.
+// The vector work issues while the matrix unit executes the wave's own
+// preceding instructions.  LDS holds K of block n+1 and V^T of block n.
+namespace pipe {
+
+constexpr int D = 128, BC = 128, T = 8, UK = 8, UV = 8, KBYTES = BC * D;
+constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
+
+__device__ __forceinline__ void fill_k(const __amdgpu_buffer_rsrc_t krs, int blk, int wv, const uint32_t* koff,
+                                       uint8_t* kbuf) {
+  const uint32_t kblk = static_cast<uint32_t>(blk) * (BC * D);
+#pragma unroll
+  for (int e = 0; e < KI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI + e)), 16, koff[e], kblk, 0, 0);
+}
+
+__device__ __forceinline__ void fill_v(const __amdgpu_buffer_rsrc_t vrs, int blk, int wv, const uint32_t* voff,
+                                       uint8_t* vbuf) {
+  const uint32_t vblk = static_cast<uint32_t>(blk) * BC;
+#pragma unroll
+  for (int e = 0; e < VI; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * (wv * VI + e)), 16, voff[e], vblk, 0, 0);
+}
+
+// S^T of one query tile for the block in kt: eight 16-key MFMA tiles.
+__device__ __forceinline__ void qk(const uint8_t* kt, int kofs0, int kofs1, v8i q, v4f (&s)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    s[t] = mfma_f8(lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK), q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+}
+
+// O^T += V^T P^T of one query tile for the block in vt.
+__device__ __forceinline__ void pv(const uint8_t* vt, int vofs0, int vofs1, v8i pop, v4f (&o)[D / 16]) {
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct)
+    o[ct] = mfma_f8(lds_read_pair(vt + vofs0 + ct * 256 * UV, vt + vofs1 + ct * 256 * UV), pop, o[ct]);
+}
+
+// Per-tile running state.
+struct Tile {
+  v8i q;            // Q operand (B of S^T = K Q^T)
+  v4f s[T];         // scores, then x
+  v8i pop;          // E4M3 codes of S*p, B operand of the P.V instruction
+  v4f o[D / 16];    // O^T accumulator
+  float ms, mcp, lsum;
+  float alpha;      // rescale factor of O for the block whose P.V comes next
+  int i;            // query row of the lane
+};
+
+// Q operand of query row i (channels [32 lg, 32 lg + 32)) and empty state.
+__device__ __forceinline__ void init_tile(Tile& X, const uint8_t* q8, int bh, int Np, int i, int lg) {
+  X.i = i;
+  const uint8_t* src = q8 + (static_cast<int64_t>(bh) * Np + i) * D + 32 * lg;
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 bb = *reinterpret_cast<const uint4*>(src + 16);
+  X.q[0] = a.x; X.q[1] = a.y; X.q[2] = a.z; X.q[3] = a.w;
+  X.q[4] = bb.x; X.q[5] = bb.y; X.q[6] = bb.z; X.q[7] = bb.w;
+  X.ms = -INFINITY; X.mcp = -INFINITY; X.lsum = 0.0f; X.alpha = 0.0f;
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) X.o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Epilogue of one tile: out = acc * (v_desc / (S * l)); the lane holds
+// channels 16 ct + 4 lg + r of its query row.
+__device__ __forceinline__ void store_tile(const Tile& X, const FwdParams& p, int bh, int N, float vdesc, int lg) {
+  const int i = X.i;
+  const float l = column_sum(X.lsum);
+  const float f = vdesc / (p.S * l);
+  if (i < N) {
+    float* orow = p.out + (static_cast<int64_t>(bh) * N + i) * D;
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) {
+      const v4f o = X.o[ct] * f;
+      *reinterpret_cast<float4*>(orow + 16 * ct + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (p.lse && lg == 0) p.lse[static_cast<int64_t>(bh) * N + i] = (X.mcp + __log2f(l)) * 0.69314718055994531f;
+  }
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B..E-1.
+template <int I, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+// Keeps a value computed at this point of the instruction stream: an empty
+// register constraint, so code motion before instruction selection cannot sink
+// the computation past the scheduling fence that follows its chunk.  (Device
+// pass only; the host pass never sees AMDGPU register constraints.)
+template <typename V>
+__device__ __attribute__((always_inline)) inline void pin(V& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+}
+
+// State of one tile's softmax between its chunks.
+struct Front {
+  float m[4];       // per-lane maxima over the key tiles, per accumulator register r
+  float v;          // lane maximum, then the block max bm of the row
+  float mnew, mc, nmc;
+  float alpha;      // the block's alpha (applied to O before its P.V)
+  bool gate;
+};
+
+// The first part of the online-softmax update (softmax_front) cut into eight
+// chunks, each issued after one pair of matrix instructions.  Same operations
+// on the same values as softmax_front (the max is exact in any order), so the
+// results are bit-identical; O is rescaled separately (rescale_o), right
+// before the block's P.V instruction of each O tile.
+//   0-2: block max over the key tiles;  3-4: across the lane groups, new
+//   running max;  5: alpha, l rescaled;  4-7: x = fma(s, c, -mc);  7: gate of
+//   the exp screen.
+template <int K, bool MASK, bool CAUSAL, bool TILES>
+__device__ __attribute__((always_inline)) inline void front_step(Front& f, Tile& X, const float c, const int jb,
+                                                                 const int N, const FwdParams& p) {
+  if constexpr (K == 0) {
+    if constexpr (MASK) {
+      const int lim = min(N, CAUSAL ? X.i + 1 : N) - jb;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X.s[t][r] = (4 * t + r < lim) ? X.s[t][r] : -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f.m[r] = fmax_nan(fmax_nan(X.s[0][r], X.s[1][r]), X.s[2][r]);
+      pin(f.m[r]);
+    }
+  } else if constexpr (K == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f.m[r] = fmax_nan(fmax_nan(f.m[r], X.s[3][r]), X.s[4][r]);
+      pin(f.m[r]);
+    }
+  } else if constexpr (K == 2) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f.m[r] = fmax_nan(fmax_nan(f.m[r], X.s[5][r]), X.s[6][r]);
+      pin(f.m[r]);
+    }
+  } else if constexpr (K == 3) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f.m[r] = fmax_nan(f.m[r], X.s[7][r]);
+    const float v = fmax_nan(fmax_nan(f.m[0], f.m[1]), fmax_nan(f.m[2], f.m[3]));
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    f.v = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    pin(f.v);
+  } else if constexpr (K == 4) {
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.v), __float_as_uint(f.v), false, false);
+    const float bm = fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    f.v = bm;
+    f.mnew = fmax_nan(X.ms, bm);
+    if constexpr (TILES) {
+      const float bmc = (bm == -INFINITY) ? -INFINITY : bm * c;
+      f.mc = (f.mnew == -INFINITY) ? 0.0f : ((X.ms == -INFINITY) ? bmc : fmax_nan(X.mcp, bmc));
+    } else {
+      f.mc = (f.mnew == -INFINITY) ? 0.0f : f.mnew * c;
+    }
+    f.nmc = -f.mc;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X.s[t][r] = __builtin_fmaf(X.s[t][r], c, f.nmc);
+      pin(X.s[t]);
+    }
+  } else if constexpr (K == 5) {
+    f.alpha = (X.ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(X.mcp - f.mc);
+    X.lsum = X.lsum * f.alpha;
+    X.ms = f.mnew;
+    X.mcp = f.mc;
+    pin(X.lsum);
+    pin(f.alpha);
+#pragma unroll
+    for (int t = 2; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X.s[t][r] = __builtin_fmaf(X.s[t][r], c, f.nmc);
+      pin(X.s[t]);
+    }
+  } else if constexpr (K == 6) {
+#pragma unroll
+    for (int t = 4; t < 6; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X.s[t][r] = __builtin_fmaf(X.s[t][r], c, f.nmc);
+      pin(X.s[t]);
+    }
+  } else {
+#pragma unroll
+    for (int t = 6; t < 8; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X.s[t][r] = __builtin_fmaf(X.s[t][r], c, f.nmc);
+      pin(X.s[t]);
+    }
+    f.gate = __any(__builtin_fmaf(f.v, c, f.nmc) >= p.xcheck);
+  }
+}
+
+// O tile ct of one query tile rescaled by the alpha of the block whose P.V
+// comes next (exactly 1 when the max did not move, 0 before the first block).
+__device__ __attribute__((always_inline)) inline void rescale_o(Tile& X, int ct) {
+  X.o[ct] *= X.alpha;
+  pin(X.o[ct]);
+}
+
+// The whole O of a tile rescaled, skipped when alpha is 1 in every row of the
+// tile (no row's max moved: multiplying by 1 changes no bit).
+__device__ __attribute__((always_inline)) inline void rescale_o_if_moved(Tile& X) {
+  if (__any(X.alpha != 1.0f)) {
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) X.o[ct] *= X.alpha;
+  }
+}
+
+// The last part (softmax_back) cut into eight chunks: chunk t takes p = 2^x
+// and the codes of key tile t; the lane's row sum is added in cast_tile's
+// pairwise order.
+template <int K, bool MASK, bool POW2>
+__device__ __attribute__((always_inline)) inline void back_step(float (&part)[T], Tile& X, const FwdParams& p) {
+  float pr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(MASK ? __builtin_fmaxf(X.s[K][r], -INFINITY) : X.s[K][r]);
+  part[K] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  uint32_t w = __float_as_uint(pr[0]);
+  if constexpr (POW2) {
+    w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
+    w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
+  } else {
+    w = e4m3_pack2<false>(pr[0] * p.S, pr[1] * p.S, w);
+    w = e4m3_pack2<true>(pr[2] * p.S, pr[3] * p.S, w);
+  }
+  X.pop[K] = static_cast<int>(w);
+  pin(w);
+  if constexpr (K >= 4) part[K - 4] = part[K - 4] + part[K];
+  pin(part[K >= 4 ? K - 4 : K]);
+  if constexpr (K == 7) {
+    part[0] = part[0] + part[2];
+    part[1] = part[1] + part[3];
+    part[0] = part[0] + part[1];
+    X.lsum = X.lsum + part[0];
+    pin(X.lsum);
+  }
+}
+
+}  // namespace pipe
+
+template <bool CAUSAL, bool POW2, bool TILES>
+__global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p) {
+  using namespace pipe;
+  constexpr int QROWS = 128;
+  constexpr int KPL = BC / 4;
+  __shared__ __align__(16) uint8_t klds[2 * KBYTES];
+  __shared__ __align__(16) uint8_t vlds[2 * KBYTES];
+
+  // ---- workgroup -> (batch*head, query tile), as k_attn_fwd
+  const int BH = p.B * p.hq;
+  const int nqt = p.n_qtiles;
+  int bh, qtile;
+  {
+    const int wg = blockIdx.x;
+    if (BH % 8 == 0) {
+      const int xcd = wg % 8, w = wg / 8, hpx = BH / 8;
+      bh = xcd * hpx + w % hpx;
+      qtile = nqt - 1 - w / hpx;
+    } else {
+      bh = wg % BH;
+      qtile = nqt - 1 - wg / BH;
+    }
+  }
+  const int b = bh / p.hq, h = bh % p.hq;
+  const int g = h / (p.hq / p.hkv);
+  const int bg = b * p.hkv + g;
+  const int N = p.N, Np = p.Np;
+  const int q0 = qtile * QROWS;
+  const float qd = TILES ? p.q_desc[static_cast<int64_t>(bh) * nqt + qtile] : p.q_desc[bh];
+  const float c_head = TILES ? 0.0f : (qd * p.k_desc[bg]) * p.ls2;
+  const float vdesc = p.v_desc[bg];
+
+  const int tid = threadIdx.x, lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n16 = lane & 15, lg = lane >> 4;
+  const int wrow0 = q0 + wv * 32;
+
+  Tile A, B;
+  init_tile(A, p.q8, bh, Np, wrow0 + n16, lg);
+  init_tile(B, p.q8, bh, Np, wrow0 + 16 + n16, lg);
+  const int kofs0 = 16 * (n16 * UK + ((2 * lg) ^ swz<UK>(n16)));
+  const int kofs1 = 16 * (n16 * UK + ((2 * lg + 1) ^ swz<UK>(n16)));
+  const int vofs0 = 16 * (n16 * UV + ((2 * lg) ^ swz<UV>(n16)));
+  const int vofs1 = 16 * (n16 * UV + ((2 * lg + 1) ^ swz<UV>(n16)));
+
+  const int q_last = min(q0 + QROWS - 1, N - 1);
+  const int J = CAUSAL ? q_last / BC : (N - 1) / BC;
+  const uint32_t head_bytes = static_cast<uint32_t>(Np) * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k8 + static_cast<int64_t>(bg) * Np * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v8t + static_cast<int64_t>(bg) * D * Np, head_bytes);
+  uint32_t koff[KI], voff[VI];
+  fill_offsets<D, BC>(wv, lane, Np, koff, voff);
+
+  // block visited at step it, its logit factor and whether the wave must mask it
+  auto blk_of = [&](int it) { return p.kv_order ? J - it : it; };
+  auto c_of = [&](int blk) {
+    return TILES ? (qd * p.k_desc[static_cast<int64_t>(bg) * nqt + blk]) * p.ls2 : c_head;
+  };
+  auto masked = [&](int blk) {
+    const int j0 = blk * BC;
+    return (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > wrow0);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  // Non-interleaved forms (first and last step).
+  auto front_all = [&](Tile& X, Front& f, int blk, auto maskc) __attribute__((always_inline)) {
+    constexpr bool M = decltype(maskc)::value;
+    const float c = c_of(blk);
+    const int jb = blk * BC + KPL * lg;
+    static_for<0, T>([&](auto kc) __attribute__((always_inline)) {
+      front_step<decltype(kc)::value, M, CAUSAL, TILES>(f, X, c, jb, N, p);
+    });
+    X.alpha = f.alpha;
+    if (f.gate) softmax_screen<T>(X.s, p);
+  };
+  auto back_all = [&](Tile& X, auto maskc) __attribute__((always_inline)) {
+    constexpr bool M = decltype(maskc)::value;
+    float part[T];
+    static_for<0, T>([&](auto kc) __attribute__((always_inline)) {
+      back_step<decltype(kc)::value, M, POW2>(part, X, p);
+    });
+  };
+  auto front_first = [&](int blk) __attribute__((always_inline)) {
+    Front fa, fb;
+    if (masked(blk)) {
+      front_all(A, fa, blk, yes{});
+      front_all(B, fb, blk, yes{});
+    } else {
+      front_all(A, fa, blk, no{});
+      front_all(B, fb, blk, no{});
+    }
+  };
+
+  // ---- first block: K tile, Q.K^T of both tiles (one K read serves both),
+  // the front of both softmaxes
+  fill_k(krs, blk_of(0), wv, koff, klds);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (J >= 1) fill_k(krs, blk_of(1), wv, koff, klds + KBYTES);
+  fill_v(vrs, blk_of(0), wv, voff, vlds);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const v8i a = lds_read_pair(klds + kofs0 + t * 256 * UK, klds + kofs1 + t * 256 * UK);
+    A.s[t] = mfma_f8(a, A.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    B.s[t] = mfma_f8(a, B.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+  }
+  front_first(blk_of(0));
+
+  // ---- step it = 0 .. J-1: back of block it's softmax under Q.K^T of block
+  // it+1, then P.V of block it under the front of block it+1's softmax.  MB /
+  // MF: block it / it+1 is the one block that needs masking (the diagonal
+  // block, or the block holding key N-1); it is always first or last in the
+  // visit order, so only the first or the last step instantiates a masked form.
+  auto step = [&](int it, auto mask_back, auto mask_front) __attribute__((always_inline)) {
+    constexpr bool MB = decltype(mask_back)::value, MF = decltype(mask_front)::value;
+    // K of block it+1 and V^T of block it have landed (every wave's share,
+    // after the barrier), and every wave is done with the buffers refilled here
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (it + 2 <= J) fill_k(krs, blk_of(it + 2), wv, koff, klds + (it & 1) * KBYTES);
+    fill_v(vrs, blk_of(it + 1), wv, voff, vlds + ((it + 1) & 1) * KBYTES);
+    // O by block it's alpha before its P.V below (the previous P.V has completed)
+    rescale_o_if_moved(A);
+    rescale_o_if_moved(B);
+    const uint8_t* kt = klds + ((it + 1) & 1) * KBYTES;
+    const uint8_t* vt = vlds + (it & 1) * KBYTES;
+    const int bn = blk_of(it + 1);
+    const float cn = c_of(bn);
+    const int jbn = bn * BC + KPL * lg;
+    // Pairs n = 0..15 of matrix instructions, both tiles sharing operand n:
+    //   0-7  Q.K^T of key tile n for block it+1, after the back chunk n of
+    //        block it's softmax (which frees the x registers the scores land in)
+    //   8-15 P.V of V^T tile n-8 for block it (O tile rescaled first), then the
+    //        front chunk n-8 of block it+1's softmax
+    // Operand n is read from LDS two pairs ahead into ops[n % 3]; a scheduling
+    // fence keeps each pair with its vector chunk.
+    auto read_op = [&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      if constexpr (n < 8) return lds_read_pair(kt + kofs0 + n * 256 * UK, kt + kofs1 + n * 256 * UK);
+      else return lds_read_pair(vt + vofs0 + (n - 8) * 256 * UV, vt + vofs1 + (n - 8) * 256 * UV);
+    };
+    v8i ops[3];
+    Front fa, fb;
+    float pa[T], pb[T];
+    ops[0] = read_op(std::integral_constant<int, 0>{});
+    ops[1] = read_op(std::integral_constant<int, 1>{});
+    static_for<0, 16>([&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int j = n % 8;
+      if constexpr (n + 2 < 16) ops[(n + 2) % 3] = read_op(std::integral_constant<int, n + 2>{});
+      if constexpr (n < 8) {
+        back_step<j, MB, POW2>(pa, A, p);
+        back_step<j, MB, POW2>(pb, B, p);
+        A.s[j] = mfma_f8(ops[n % 3], A.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        B.s[j] = mfma_f8(ops[n % 3], B.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      } else {
+        A.o[j] = mfma_f8(ops[n % 3], A.pop, A.o[j]);
+        B.o[j] = mfma_f8(ops[n % 3], B.pop, B.o[j]);
+        front_step<j, MF, CAUSAL, TILES>(fa, A, cn, jbn, N, p);
+        front_step<j, MF, CAUSAL, TILES>(fb, B, cn, jbn, N, p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    A.alpha = fa.alpha;
+    B.alpha = fb.alpha;
+    if (fa.gate) softmax_screen<T>(A.s, p);
+    if (fb.gate) softmax_screen<T>(B.s, p);
+  };
+  const bool first_masked = masked(blk_of(0));
+  const bool last_masked = J >= 1 && masked(blk_of(J));
+  int it = 0;
+  if (J >= 1 && first_masked) {
+    step(0, yes{}, no{});
+    it = 1;
+  }
+  const int fast_end = last_masked ? J - 2 : J - 1;
+  for (; it <= fast_end; ++it) step(it, no{}, no{});
+  if (last_masked && it == J - 1) step(J - 1, no{}, yes{});
+
+  // ---- last block: back of its softmax, P.V of both tiles
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (masked(blk_of(J))) {
+    back_all(A, yes{});
+    back_all(B, yes{});
+  } else {
+    back_all(A, no{});
+    back_all(B, no{});
+  }
+  {
+    const uint8_t* vt = vlds + (J & 1) * KBYTES;
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct) {
+      const v8i a = lds_read_pair(vt + vofs0 + ct * 256 * UV, vt + vofs1 + ct * 256 * UV);
+      rescale_o(A, ct);
+      rescale_o(B, ct);
+      A.o[ct] = mfma_f8(a, A.pop, A.o[ct]);
+      B.o[ct] = mfma_f8(a, B.pop, B.o[ct]);
+    }
+  }
+
+  // ---- epilogue
+  store_tile(A, p, bh, N, vdesc, lg);
+  store_tile(B, p, bh, N, vdesc, lg);
+}
+
 // -------------------------------------------------------- P-cast-only path
 // Binary32 Q/K/V, only P cast (the P-Cast summary's simulation that follows
 // the kernel step by step, Bijdragen item 4).  One thread per query row; the score is an
@@ -580,6 +1071,13 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
 template <int D, int BC, bool CAUSAL, bool POW2, bool DUMP>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.B * p.hq * p.n_qtiles));
+  if constexpr (D == 128 && BC == 128 && !DUMP) {
+    if (!p.int8 && !p.no_pipe) {
+      if (p.tiles) k_attn_fwd_pipe<CAUSAL, POW2, true><<<grid, dim3(kThreads), 0, st>>>(p);
+      else k_attn_fwd_pipe<CAUSAL, POW2, false><<<grid, dim3(kThreads), 0, st>>>(p);
+      return hipGetLastError();
+    }
+  }
   if (p.tiles) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, true, false><<<grid, dim3(kThreads), 0, st>>>(p);
   else if (p.int8) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false, true><<<grid, dim3(kThreads), 0, st>>>(p);
   else k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false, false><<<grid, dim3(kThreads), 0, st>>>(p);
