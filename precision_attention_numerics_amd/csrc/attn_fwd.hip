@@ -601,6 +601,8 @@ __device__ __forceinline__ void init_tile(Tile& X, const uint8_t* q8, int bh, in
   X.q[4] = bb.x; X.q[5] = bb.y; X.q[6] = bb.z; X.q[7] = bb.w;
   X.ms = -INFINITY; X.mcp = -INFINITY; X.lsum = 0.0f; X.alpha = 0.0f;
 #pragma unroll
+  for (int t = 0; t < T; ++t) X.pop[t] = 0;
+#pragma unroll
   for (int ct = 0; ct < D / 16; ++ct) X.o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
@@ -658,7 +660,10 @@ struct Front {
 //   0-2: block max over the key tiles;  3-4: across the lane groups, new
 //   running max;  5: alpha, l rescaled;  4-7: x = fma(s, c, -mc);  7: gate of
 //   the exp screen.
-template <int K, bool MASK, bool CAUSAL, bool TILES>
+// FIRST: the first block visited.  Every row has a visible key in it (the
+// diagonal block holds key 128*qtile, block 0 holds key 0), so after it the
+// running max is finite and the -inf cases of mc and alpha cannot occur.
+template <int K, bool MASK, bool CAUSAL, bool TILES, bool FIRST = true>
 __device__ __attribute__((always_inline)) inline void front_step(Front& f, Tile& X, const float c, const int jb,
                                                                  const int N, const FwdParams& p) {
   if constexpr (K == 0) {
@@ -698,7 +703,9 @@ __device__ __attribute__((always_inline)) inline void front_step(Front& f, Tile&
     const float bm = fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
     f.v = bm;
     f.mnew = fmax_nan(X.ms, bm);
-    if constexpr (TILES) {
+    if constexpr (!FIRST) {
+      f.mc = TILES ? fmax_nan(X.mcp, bm * c) : f.mnew * c;
+    } else if constexpr (TILES) {
       const float bmc = (bm == -INFINITY) ? -INFINITY : bm * c;
       f.mc = (f.mnew == -INFINITY) ? 0.0f : ((X.ms == -INFINITY) ? bmc : fmax_nan(X.mcp, bmc));
     } else {
@@ -712,7 +719,7 @@ __device__ __attribute__((always_inline)) inline void front_step(Front& f, Tile&
       pin(X.s[t]);
     }
   } else if constexpr (K == 5) {
-    f.alpha = (X.ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(X.mcp - f.mc);
+    f.alpha = (FIRST && X.ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(X.mcp - f.mc);
     X.lsum = X.lsum * f.alpha;
     X.ms = f.mnew;
     X.mcp = f.mc;
@@ -767,7 +774,10 @@ __device__ __attribute__((always_inline)) inline void back_step(float (&part)[T]
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(MASK ? __builtin_fmaxf(X.s[K][r], -INFINITY) : X.s[K][r]);
   part[K] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  uint32_t w = __float_as_uint(pr[0]);
+  // both halves of w are written below; its initial bits are the previous
+  // block's codes of this key tile (dead by now: that P.V has been issued), so
+  // the loop keeps the codes in one register and no copy is needed
+  uint32_t w = static_cast<uint32_t>(X.pop[K]);
   if constexpr (POW2) {
     w = e4m3_pack2_pow2<false>(pr[0], pr[1], p.inv_S, w);
     w = e4m3_pack2_pow2<true>(pr[2], pr[3], p.inv_S, w);
@@ -775,8 +785,8 @@ __device__ __attribute__((always_inline)) inline void back_step(float (&part)[T]
     w = e4m3_pack2<false>(pr[0] * p.S, pr[1] * p.S, w);
     w = e4m3_pack2<true>(pr[2] * p.S, pr[3] * p.S, w);
   }
-  X.pop[K] = static_cast<int>(w);
   pin(w);
+  X.pop[K] = static_cast<int>(w);
   if constexpr (K >= 4) part[K - 4] = part[K - 4] + part[K];
   pin(part[K >= 4 ? K - 4 : K]);
   if constexpr (K == 7) {
@@ -947,8 +957,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
       } else {
         A.o[j] = mfma_f8(ops[n % 3], A.pop, A.o[j]);
         B.o[j] = mfma_f8(ops[n % 3], B.pop, B.o[j]);
-        front_step<j, MF, CAUSAL, TILES>(fa, A, cn, jbn, N, p);
-        front_step<j, MF, CAUSAL, TILES>(fb, B, cn, jbn, N, p);
+        front_step<j, MF, CAUSAL, TILES, false>(fa, A, cn, jbn, N, p);
+        front_step<j, MF, CAUSAL, TILES, false>(fb, B, cn, jbn, N, p);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
