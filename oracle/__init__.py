@@ -24,12 +24,14 @@ What it computes (each function cites the passage it follows):
   unrotated (study page, "What do these scores mean?").
 
 Every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, invariants, brute force or printed values.  Parity
-unpinned against the pages: the shared-key illustration, whose vectors the
-page does not print, and the matrix-unit score model of :func:`fp8_dot128`
-(``mode="mfma"``), which the pages do not describe; it is held by invariants
-(the exact sum when nothing is truncated, symmetry in its operands, an error
-bound), not by a printed value.
+against closed forms, invariants, brute force or printed values.  The
+matrix-unit score model of :func:`fp8_dot128` (``mode="mfma"``) is not
+described by the pages (they fix only the E4M3 codec); it is pinned by cases
+whose scores are derived by hand from each of its rules (pass order, group
+truncation quantum, pass and running floors, per-pass rounding, sign of the
+floor), and each plausible mistake in those rules is shown to fail one of them
+(tests/test_oracle_score_model.py).  Parity unpinned against the pages: the
+shared-key illustration's FP8 weights, whose vectors the page does not print.
 """
 from __future__ import annotations
 
