@@ -201,3 +201,18 @@ def long_context(seed: int = 400, N: int = 32768, hq: int = 32, hkv: int = 8, d:
     v = round_bf16(g.standard_normal((1, hkv, N, d), dtype=np.float32))
     return Workload("long_context", q, k, v, "bf16", True, 128, 256.0, 1, ("rotated", "centered_rotated"),
                     rotation_signs(d), dict(seed=seed, N=N, hq=hq, hkv=hkv, d=d, delta=delta, n_sink=4))
+
+
+def shared_key_vectors(seed: int, d: int = 8, keys: int = 4, grid: int = 8):
+    """One query and `keys` keys of `d` channels for the study page's shared-key
+    illustration ("01 / Synthetic illustration": four keys, eight channels).
+    Entries are N(0,1) rounded to multiples of 2^-grid, so that adding an
+    integer shared coordinate, averaging the keys and subtracting the mean
+    are exact in binary32.  Returns (q [d], K [keys, d], signs [d]) as float32
+    / int8; the shared first coordinate is added by the caller."""
+    g = rng(seed)
+    scale = float(2 ** grid)
+    q = (np.round(g.standard_normal(d) * scale) / scale).astype(np.float32)
+    K = (np.round(g.standard_normal((keys, d)) * scale) / scale).astype(np.float32)
+    signs = np.where(g.random(d) < 0.5, -1, 1).astype(np.int8)
+    return q, K, signs
