@@ -187,3 +187,51 @@ def test_header_is_plain_c_and_links_from_c(tmp_path):
                     str(src), "-L", libdir, "-lfp8attn", "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
     assert out == ["128", "1"]
+
+
+def _build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_fp8attn_build_for_test", os.path.join(ROOT, "precision_attention_numerics_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_library_built_from_these_sources(lib):
+    """The in-tree library reports the hash of the sources it was compiled
+    from; it must be the hash of the sources in this tree (a stale or foreign
+    binary fails here)."""
+    lib.fp8_attn_build_info.restype = ctypes.c_char_p
+    info = lib.fp8_attn_build_info().decode()
+    assert info == f"source_sha256={_build_module().source_hash()} arch=gfx950", info
+
+
+def test_build_from_a_clean_checkout(tmp_path):
+    """__graft_entry__.build() on the committed tree alone (git archive of
+    HEAD: no built library, no working files) compiles the HIP library and the
+    oracle, after which the package imports and the library reports the
+    checkout's source hash."""
+    import shutil
+    import subprocess
+    import sys
+    if shutil.which("git") is None or not os.path.isdir(os.path.join(ROOT, ".git")):
+        pytest.skip("needs the git repository")
+    if shutil.which("/opt/rocm/bin/hipcc") is None and shutil.which("hipcc") is None:
+        pytest.skip("needs hipcc")
+    archive = subprocess.run(["git", "-C", ROOT, "archive", "HEAD"], check=True, capture_output=True).stdout
+    subprocess.run(["tar", "-x", "-C", str(tmp_path)], input=archive, check=True)
+    assert not os.path.exists(tmp_path / "precision_attention_numerics_amd" / "libfp8attn.so")
+    code = ("import __graft_entry__ as g; g.build(); import precision_attention_numerics_amd as p, ctypes; "
+            "p._abi._lib.fp8_attn_build_info.restype = ctypes.c_char_p; "
+            "print('BUILD_INFO', p._abi._lib.fp8_attn_build_info().decode()); print('STATUS', p.strerror(0))")
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    res = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=900, env=env)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = dict(l.split(" ", 1) for l in res.stdout.splitlines() if l.startswith(("BUILD_INFO", "STATUS")))
+    assert lines["STATUS"] == "ok"
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_clean_build", tmp_path / "precision_attention_numerics_amd" / "build.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert lines["BUILD_INFO"] == f"source_sha256={mod.source_hash()} arch=gfx950"
