@@ -88,6 +88,11 @@ def _load():
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
                                       _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int]
     lib.orc_attention_fp8_tiles.argtypes = lib.orc_attention_fp8.argtypes
+    lib.orc_attention_fp8_rowhash.argtypes = [_c_u8p, _c_u8p, _c_u8p, _c_f32p, _c_f32p, _c_f32p,
+                                              _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
+                                              ctypes.POINTER(ctypes.c_uint64), _c_u32p, ctypes.c_int32,
+                                              ctypes.c_int, ctypes.c_int]
     lib.orc_attention_pcast_f32.argtypes = [_c_f32p, _c_f32p, _c_f32p,
                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
@@ -290,6 +295,36 @@ def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: f
             _threads(nthreads))
     _check(rc, "attention_fp8")
     return LoopResult(out, p, z)
+
+
+def attention_fp8_rowhash(prep: Prepared, softmax_scale: float | None = None, p_scale: float = 256.0,
+                          kv_order: int = 0, block_n: int = 128, causal: bool = True, rows=None,
+                          k_sink: int = 0, score_mode: str = "mfma", nthreads: int | None = None):
+    """The main loop's P~ codes only (per-head scales): per row the checksum
+    row_hash(P~ row) and the count of zero codes among keys >= k_sink, without
+    accumulating the output.  Returns (row_hash [B,Hq,nrows] uint64,
+    row_zeros [B,Hq,nrows] uint32)."""
+    if prep.tiles:
+        raise ValueError("per-head scales only")
+    B, Hq, N, d = prep.q8.shape
+    Hkv = prep.k8.shape[1]
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(1.0 / np.sqrt(d)))
+    r, nrows = _rows_arg(rows, N)
+    h = np.empty((B, Hq, nrows), np.uint64)
+    z = np.empty((B, Hq, nrows), np.uint32)
+    if prep.int8:
+        score_mode = "int8"
+    rc = _load().orc_attention_fp8_rowhash(
+        _p(prep.q8, _c_u8p), _p(prep.k8, _c_u8p), _p(prep.v8, _c_u8p),
+        _p(np.ascontiguousarray(prep.q_desc, np.float32), _c_f32p),
+        _p(np.ascontiguousarray(prep.k_desc, np.float32), _c_f32p),
+        _p(np.ascontiguousarray(prep.v_desc, np.float32), _c_f32p),
+        B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale), int(kv_order), int(block_n), int(causal),
+        _p(r, _c_i32p), nrows, h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), _p(z, _c_u32p), int(k_sink),
+        SCORE_MODES[score_mode], _threads(nthreads))
+    _check(rc, "attention_fp8_rowhash")
+    return h, z
 
 
 def attention_pcast_f32(q, k, v, softmax_scale: float | None = None, p_scale: float = 256.0,

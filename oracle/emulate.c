@@ -246,11 +246,22 @@ typedef struct {
   float softmax_scale, p_scale;
   int kv_order, block_n, causal, score_mode, p_cast, tiles;
   const int32_t* rows;
-  float* out;
+  float* out;          /* NULL: no output (the P~ codes, counts and checksums only) */
   uint8_t* p_out;
   uint32_t* row_zeros;
+  uint64_t* row_hash;
   int32_t k_sink;
 } loop_args;
+
+/* Weight of key j in the P~ row checksum: the (j+1)-th output of the
+ * splitmix64 generator seeded with 0 (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014), made odd. */
+static uint64_t key_weight(int64_t j) {
+  uint64_t z = (uint64_t)(j + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (z ^ (z >> 31)) | 1ull;
+}
 
 /* log2(e) to binary64 precision. */
 #define LOG2E 1.4426950408889634
@@ -304,6 +315,7 @@ static void attn_row(void* p, int64_t item, double* scratch) {
   uint8_t* prow = a->p_out ? a->p_out + (bh * a->nrows + r) * N : NULL;
   if (prow) memset(prow, 0, (size_t)N);
   uint32_t zeros = 0;
+  uint64_t hash = 0;
   float S = a->p_scale;
 
   for (int64_t t = 0; t <= J; ++t) {
@@ -326,7 +338,8 @@ static void attn_row(void* p, int64_t item, double* scratch) {
       alpha = (ms == -INFINITY) ? 0.0f : orc_exp2_rn32(mc_prev - mc);
     }
     l = l * alpha;
-    for (int64_t cc = 0; cc < d; ++cc) acc[cc] = acc[cc] * alpha;
+    if (a->out)
+      for (int64_t cc = 0; cc < d; ++cc) acc[cc] = acc[cc] * alpha;
     for (int64_t j = j0; j < j1; ++j) {
       float x = fmaf((float)s[j], c, -mc);
       float pj = orc_exp2_rn32(x);
@@ -335,11 +348,13 @@ static void attn_row(void* p, int64_t item, double* scratch) {
         uint8_t code = orc_e4m3_encode(S * pj);
         if (prow) prow[j] = code;
         if (j >= a->k_sink && code == 0) ++zeros;
+        hash += (uint64_t)code * key_weight(j);
         pt = orc_e4m3_decode(code);
       } else {
         pt = S * pj;
       }
       l = l + pj;
+      if (!a->out) continue;
       if (fp8) {
         const uint8_t* vr = a->v8 + (bg * N + j) * d;
         for (int64_t cc = 0; cc < d; ++cc) acc[cc] = acc[cc] + pt * orc_e4m3_decode(vr[cc]);
@@ -351,11 +366,14 @@ static void attn_row(void* p, int64_t item, double* scratch) {
     if (!a->tiles) ms = mnew;
     mc_prev = mc;
   }
-  float vd = fp8 ? a->v_desc[bg] : 1.0f;
-  float f = vd / (S * l);
-  float* o = a->out + (bh * a->nrows + r) * d;
-  for (int64_t cc = 0; cc < d; ++cc) o[cc] = acc[cc] * f;
+  if (a->out) {
+    float vd = fp8 ? a->v_desc[bg] : 1.0f;
+    float f = vd / (S * l);
+    float* o = a->out + (bh * a->nrows + r) * d;
+    for (int64_t cc = 0; cc < d; ++cc) o[cc] = acc[cc] * f;
+  }
   if (a->row_zeros) a->row_zeros[bh * a->nrows + r] = zeros;
+  if (a->row_hash) a->row_hash[bh * a->nrows + r] = hash;
 }
 
 static int check_loop(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float p_scale,
@@ -384,6 +402,27 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
   a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
   a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.rows = rows; a.out = out;
   a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
+  return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
+}
+
+int orc_attention_fp8_rowhash(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                              const float* q_desc, const float* k_desc, const float* v_desc,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                              float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
+                              const int32_t* rows, int64_t nrows,
+                              uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink,
+                              int score_mode, int nthreads) {
+  if (!q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc || !row_hash || d > 128) return -1;
+  if (!rows) nrows = N;
+  int rc = check_loop(B, Hq, Hkv, N, d, p_scale, kv_order, block_n, rows, nrows);
+  if (rc) return rc;
+  loop_args a;
+  memset(&a, 0, sizeof a);
+  a.q8 = q8; a.k8 = k8; a.v8 = v8; a.q_desc = q_desc; a.k_desc = k_desc; a.v_desc = v_desc;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
+  a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
+  a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.rows = rows; a.out = NULL;
+  a.row_hash = row_hash; a.row_zeros = row_zeros; a.k_sink = k_sink;
   return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
 }
 

@@ -90,6 +90,18 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                       float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
                       int score_mode, int nthreads);
 
+/* The main loop of orc_attention_fp8 for its P~ codes only: per row the
+ * checksum sum_j code_j * W_j mod 2^64 (W_j = splitmix64 output j+1 from seed
+ * 0, made odd) and the count of zero codes among keys j >= k_sink; the output
+ * accumulation is skipped. */
+int orc_attention_fp8_rowhash(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                              const float* q_desc, const float* k_desc, const float* v_desc,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                              float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
+                              const int32_t* rows, int64_t nrows,
+                              uint64_t* row_hash, uint32_t* row_zeros, int32_t k_sink,
+                              int score_mode, int nthreads);
+
 /* Main loop with per-tile Q/K descales (from a TILE prologue); block_n must
  * divide 128.  The logit factor c depends on the row's query tile and the
  * block's key tile, so the running max is kept in scaled units: per block

@@ -2,6 +2,7 @@
 the splitmix64 reference outputs, odd weights, order independence, and that
 any single changed code changes the sum."""
 import numpy as np
+import pytest
 
 import oracle
 
@@ -55,3 +56,22 @@ def test_every_single_code_change_detected():
             r = row.copy()
             r[j] = new
             assert oracle.row_hash(r) != h0
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("causal", [True, False])
+def test_checksum_only_path_matches_the_dump(orc, order, causal):
+    """attention_fp8_rowhash (no output accumulation, checksum and zero count
+    in C) gives the checksums of the full loop's P~ dump and its counts."""
+    import synth
+    w = synth.qwen_like(1, 4, 2, 64, seed=5, N=333, texts=1)
+    op = orc.prepare(w.q, w.k, w.v, signs=w.signs, rotate=True, center=True)
+    for bn in (64, 128):
+        full = orc.attention_fp8(op, p_scale=256.0, kv_order=order, block_n=bn, causal=causal, want_p=True, k_sink=4)
+        h, z = orc.attention_fp8_rowhash(op, p_scale=256.0, kv_order=order, block_n=bn, causal=causal, k_sink=4)
+        assert np.array_equal(h, orc.row_hash(full.p))
+        assert np.array_equal(z, full.row_zeros)
+        rows = np.array([0, 5, 332, 128], np.int32)
+        hs, zs = orc.attention_fp8_rowhash(op, p_scale=256.0, kv_order=order, block_n=bn, causal=causal, rows=rows,
+                                           k_sink=4)
+        assert np.array_equal(hs, h[:, :, rows]) and np.array_equal(zs, z[:, :, rows])
