@@ -54,12 +54,15 @@ typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3, FP8A_I8
  * with FA3's full-sequence per-head scales; V keeps per-head scales.  Codes
  * prepared this way go to fp8_attn_fwd_tile_scaled. */
 #define FP8A_TILE_SCALES 4u
-/* PREFIX_SCALES (with TILE_SCALES, without CENTER_K): tile t's Q and K scales
- * come from the largest tile maximum among tiles 0..t, so no scale depends on
- * tokens past its own tile (the project page notes that full-sequence means
- * and scales see future tokens).  Causal at the 128-token tile granularity.
- * Errors: FP8A_ERR_PARAM without TILE_SCALES, FP8A_ERR_UNSUPPORTED with
- * CENTER_K (one set of K codes cannot carry a per-query prefix mean). */
+/* PREFIX_SCALES (with TILE_SCALES): tile t's Q and K scales come from the
+ * largest tile maximum among tiles 0..t, so no scale depends on tokens past
+ * its own tile (the project page notes that full-sequence means and scales see
+ * future tokens).  With CENTER_K the mean key is taken over the first
+ * 128-token tile only (min(N, 128) tokens): one shift common to every key, so
+ * exact softmax is unchanged, that depends on no token past tile 0.  Every
+ * quantity used for tile t then depends only on tokens in tiles 0..t: causal
+ * at the 128-token tile granularity.  Error: FP8A_ERR_PARAM without
+ * TILE_SCALES. */
 #define FP8A_PREFIX_SCALES 8u
 /* INT8_QK: Q and K become two's-complement int8 codes, clamp(RNE(x * 127/A),
  * -127, 127), with descale A/127 (times RN32(1/sqrt d) when rotated); V stays
@@ -91,9 +94,10 @@ size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* shape, uint32_t flags)
  * Computes, per (batch, head) over the full sequence (project page, second
  * section: independent Q/K/V scales over the full sequence for each batch and
  * head):
- *   1. if CENTER: mu[b,g,:] = mean over all N tokens of K[b,g,:,:], in binary64
- *      (chunks of 64 tokens summed in order, chunk sums added in a pairwise
- *      tree), rounded to binary32; K' = K - mu.
+ *   1. if CENTER: mu[b,g,:] = mean over all N tokens of K[b,g,:,:] (over the
+ *      first min(N, 128) with PREFIX_SCALES), in binary64 (chunks of 64 tokens
+ *      summed in order, chunk sums added in a pairwise tree), rounded to
+ *      binary32; K' = K - mu.
  *   2. if ROTATE: for Q and K' (never V) each row is multiplied by
  *      rot_signs and passed through the unnormalised Sylvester Walsh-Hadamard
  *      transform (stages h = 1, 2, ..., d/2) in binary32.

@@ -228,9 +228,10 @@ def prepare(q, k, v, rotate: bool = False, center: bool = False, signs=None, til
     """Quantisation prologue on binary32 operands (BF16 widened exactly).
     tiles: one Q/K scale per 128-token tile instead of per (batch, head) (the
     earlier emulator's granularity, attention-numerics project page, second
-    section); V keeps per-head scales.  prefix (with tiles, without center):
-    tile t's Q/K scale from the largest maximum among tiles 0..t, so no scale
-    depends on tokens past its tile.  int8: Q/K as int8 codes (scale 127/A,
+    section); V keeps per-head scales.  prefix (with tiles): tile t's Q/K scale
+    from the largest maximum among tiles 0..t, so no scale depends on tokens
+    past its tile; with center the mean key is taken over the first 128-token
+    tile only (a shift common to every key that sees no later token).  int8: Q/K as int8 codes (scale 127/A,
     round to nearest even, clamp +-127), V still E4M3."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)

@@ -80,7 +80,10 @@ int orc_prepare(const float* q, const float* k, const float* v,
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv || (d & (d - 1))) return -1;
   int rotate = (flags & ORC_ROTATE) != 0, center = (flags & ORC_CENTER) != 0;
   int tiled = (flags & ORC_TILE) != 0, prefix = (flags & ORC_PREFIX) != 0, i8 = (flags & ORC_INT8) != 0;
-  if (prefix && (!tiled || center)) return -1;
+  if (prefix && !tiled) return -1;
+  /* tokens the mean key is taken over: all N, or with prefix scales the
+   * first 128-token tile only (no key shift may depend on later tokens) */
+  int64_t n_mean = prefix ? (N < ORC_TILE_TOKENS ? N : ORC_TILE_TOKENS) : N;
   /* scale groups: the whole sequence, or 128-token tiles */
   int64_t span = tiled ? ORC_TILE_TOKENS : N, ngroup = (N + span - 1) / span;
   if (rotate && !signs) return -1;
@@ -116,7 +119,7 @@ int orc_prepare(const float* q, const float* k, const float* v,
   /* K: centre, rotate, amax, quantise.  V: amax, quantise (never rotated). */
   for (int64_t bg = 0; bg < B * Hkv; ++bg) {
     const float* src = k + bg * N * d;
-    for (int64_t c = 0; c < d; ++c) mu[c] = center ? column_mean(src, N, d, c, part) : 0.0f;
+    for (int64_t c = 0; c < d; ++c) mu[c] = center ? column_mean(src, n_mean, d, c, part) : 0.0f;
     if (center && k_mean) memcpy(k_mean + bg * d, mu, sizeof(float) * (size_t)d);
     for (int64_t n = 0; n < N; ++n) {
       for (int64_t c = 0; c < d; ++c) buf[n * d + c] = center ? src[n * d + c] - mu[c] : src[n * d + c];

@@ -31,8 +31,11 @@
 #define ORC_TILE_TOKENS 128
 /* With TILE: tile t's Q and K scales come from the largest tile maximum among
  * tiles 0..t (prefix scales: no scale depends on tokens past its tile's end,
- * the caveat the project page raises about full-sequence scales).  Not
- * combined with CENTER (one K code set cannot carry a per-query prefix mean). */
+ * the caveat the project page raises about full-sequence means and scales).
+ * With CENTER as well, the mean key is taken over the first 128-token tile
+ * only: one shift common to every key (exact softmax is unchanged by it) that
+ * depends on no token past tile 0.  So every quantity used for tile t depends
+ * only on tokens in tiles 0..t. */
 #define ORC_PREFIX 8u
 /* INT8 Q/K (the INT8-QK / FP8-PV kernel family the attention-numerics project
  * page measures, named without its quantisation): Q and K codes are

@@ -117,7 +117,6 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
     return FP8A_ERR_PARAM;
   if ((flags & FP8A_INT8_QK) && (flags & FP8A_TILE_SCALES)) return FP8A_ERR_UNSUPPORTED;
   if ((flags & FP8A_PREFIX_SCALES) && !(flags & FP8A_TILE_SCALES)) return FP8A_ERR_PARAM;
-  if ((flags & FP8A_PREFIX_SCALES) && (flags & FP8A_CENTER_K)) return FP8A_ERR_UNSUPPORTED;
   if (!q || !k || !v || !q8 || !k8 || !v8t || !q_desc || !k_desc || !v_desc) return FP8A_ERR_NULL;
   if ((flags & FP8A_ROTATE_QK) && !rot_signs) return FP8A_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
@@ -146,7 +145,10 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.amax = reinterpret_cast<uint32_t*>(ws);
   ws += align_up(static_cast<size_t>(a.B) * (a.hq * a.ntile + a.hkv * a.ntile + a.hkv) * sizeof(uint32_t));
-  a.np2 = np2_chunks(a.N);
+  // tokens the mean key is taken over: all N, or with prefix scales the first
+  // 128-token tile only (no key shift may depend on later tokens)
+  a.n_mean = a.prefix ? (a.N < 128 ? a.N : 128) : a.N;
+  a.np2 = np2_chunks(a.n_mean);
   if (a.center) {
     a.mean_part = reinterpret_cast<double*>(ws);
     ws += align_up(static_cast<size_t>(a.B) * a.hkv * a.np2 * a.D * sizeof(double));

@@ -477,8 +477,9 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   if (a.center) {
     constexpr int32_t kChunksPerBlock = 256 / (D / 8);
     k_kmean_partial<IT, D><<<dim3((a.np2 + kChunksPerBlock - 1) / kChunksPerBlock, B * hkv), dim3(256), 0, st>>>(
-        k, a.ks[0], a.ks[1], a.ks[2], hkv, N, a.np2, a.mean_part);
-    k_kmean_final<<<dim3(B * hkv, D / kMeanCh), dim3(kMeanCh * kMeanW), 0, st>>>(a.mean_part, a.np2, N, D, a.k_mean);
+        k, a.ks[0], a.ks[1], a.ks[2], hkv, a.n_mean, a.np2, a.mean_part);
+    k_kmean_final<<<dim3(B * hkv, D / kMeanCh), dim3(kMeanCh * kMeanW), 0, st>>>(a.mean_part, a.np2, a.n_mean, D,
+                                                                                  a.k_mean);
   }
   const int8_t* ks = a.rotate ? a.signs : nullptr;
   if (a.rotate && a.center) {

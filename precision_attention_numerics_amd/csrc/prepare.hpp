@@ -18,7 +18,8 @@ struct PrepareArgs {
   int32_t* status;               // may be null
   uint32_t* amax;                // workspace: B*(hq*ntile + hkv*ntile + hkv)
   double* mean_part;             // workspace: B*hkv*np2*D (CENTER only)
-  int32_t np2;                   // chunk count rounded up to a power of two
+  int32_t n_mean;                // tokens the mean key is taken over (N, or the first tile)
+  int32_t np2;                   // chunk count of those tokens rounded up to a power of two
 };
 
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t st);

@@ -107,7 +107,8 @@ def test_prepare_rejects(abi):
     assert _prep(abi, ok, flags=32) == -4                              # unknown flag
     assert _prep(abi, ok, flags=abi.FP8A_TILE_SCALES, ws_bytes=1) == -5   # tile maxima need workspace too
     assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES) == -4                # prefix scales need tiles
-    assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES | abi.FP8A_TILE_SCALES | abi.FP8A_CENTER_K) == -3
+    # a centred prefix prologue is accepted (it then fails only on the missing workspace)
+    assert _prep(abi, ok, flags=abi.FP8A_PREFIX_SCALES | abi.FP8A_TILE_SCALES | abi.FP8A_CENTER_K, ws_bytes=1) == -5
     assert _prep(abi, ok, flags=abi.FP8A_INT8_QK | abi.FP8A_TILE_SCALES) == -3         # int8 only per head
     assert _prep(abi, ok, q=None) == -1
     assert _prep(abi, ok, flags=abi.FP8A_ROTATE_QK, signs=None) == -1

@@ -92,10 +92,11 @@ def test_tiles_of_very_different_magnitude(pan, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("cond", ["plain", "rotated"])
+@pytest.mark.parametrize("cond", list(synth.CONDITIONS))
 def test_prefix_scales(pan, d, cond):
     """Prefix tile scales (tile t from the largest maximum of tiles 0..t) on
-    tiles of rising and falling magnitude."""
+    tiles of rising and falling magnitude; centred conditions take the mean key
+    over the first tile only (the mean is compared bit for bit)."""
     w = synth.qwen_like(1, 4, 2, d, seed=570 + d, N=650, texts=1)
     gains = (0.5, 4.0, 1.0, 0.25, 8.0, 2.0)
     for t in range(6):
@@ -105,13 +106,14 @@ def test_prefix_scales(pan, d, cond):
     run_tiles(pan, w, cond, kv_order=0, block_n=64, causal=False, prefix=True)
 
 
-def test_prefix_scales_ignore_future_tokens(pan):
+@pytest.mark.parametrize("center", [False, True])
+def test_prefix_scales_ignore_future_tokens(pan, center):
     """Changing tokens from tile 2 on leaves tiles 0 and 1's codes and scales
-    as they were."""
+    (and, centred, the mean key) as they were."""
     import precision_attention_numerics_amd as pan_
     w = synth.qwen_like(1, 2, 1, 128, seed=580, N=512, texts=1)
     pipe = pan_.AttnPipeline(1, 2, 1, 512, 128)
-    args = dict(rotate=True, center=False, signs=signs_dev(w), tiles=True, prefix=True)
+    args = dict(rotate=True, center=center, signs=signs_dev(w), tiles=True, prefix=True)
     a = pipe.prepare(dev(w.q, "bf16"), dev(w.k, "bf16"), dev(w.v, "bf16"), **args)
     q2, k2 = w.q.copy(), w.k.copy()
     q2[:, :, 256:] *= np.float32(8.0)
@@ -121,6 +123,8 @@ def test_prefix_scales_ignore_future_tokens(pan):
     assert torch.equal(a.q8[:, :, :256], b.q8[:, :, :256]) and torch.equal(a.k8[:, :, :256], b.k8[:, :, :256])
     qa, qb = a.q_desc.view(2, 4), b.q_desc.view(2, 4)
     assert torch.equal(qa[:, :2], qb[:, :2]) and torch.equal(a.k_desc[:2], b.k_desc[:2])
+    if center:
+        assert torch.equal(a.k_mean, b.k_mean)
 
 
 def test_equal_tile_maxima_match_the_per_head_kernel(pan):

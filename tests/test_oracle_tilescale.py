@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 T = 128
 
@@ -133,12 +134,73 @@ def test_prefix_scales_are_running_maxima_of_tile_maxima():
     assert same[0] and not same.all()
 
 
-def test_prefix_scales_reject_centering():
+def test_prefix_scales_need_tiles():
     q, k, v = operands(7, 256)
     with pytest.raises(RuntimeError):
-        oracle.prepare(q, k, v, center=True, tiles=True, prefix=True)
-    with pytest.raises(RuntimeError):
         oracle.prepare(q, k, v, prefix=True)
+    with pytest.raises(RuntimeError):
+        oracle.prepare(q, k, v, center=True, prefix=True)
+
+
+def test_prefix_mean_is_the_first_tile_mean():
+    """With prefix scales the mean key is the mean of the first 128 tokens:
+    integer-valued keys make every partial sum exact and the mean of 128
+    integers dyadic, so it is the exact rational rounded once; for N < 128 it
+    is the mean of all N tokens."""
+    g = np.random.default_rng(31)
+    for N in (640, 100):
+        k = g.integers(-1000, 1000, (1, 2, N, 64)).astype(np.float32)
+        q = g.standard_normal((1, 4, N, 64)).astype(np.float32)
+        p = oracle.prepare(q, k, k, center=True, tiles=True, prefix=True)
+        n0 = min(N, 128)
+        want = (k[:, :, :n0].astype(np.float64).sum(2) / n0).astype(np.float32)
+        assert np.array_equal(p.k_mean, want)
+        full = oracle.prepare(q, k, k, center=True)
+        assert N <= 128 or not np.array_equal(full.k_mean, p.k_mean)
+
+
+def test_prefix_mean_keeps_exact_attention():
+    """The prefix mean is one vector subtracted from every key, so ideal
+    attention on the centred keys equals ideal attention on the original keys
+    (binary64, causal and not)."""
+    q, k, v = operands(9, 384)
+    p = oracle.prepare(q, k, v, center=True, tiles=True, prefix=True)
+    kc = k.astype(np.float64) - p.k_mean[:, :, None, :].astype(np.float64)   # the shift, exact in binary64
+    for causal in (True, False):
+        np.testing.assert_allclose(oracle.attention_f64(q, kc, v, causal=causal),
+                                   oracle.attention_f64(q, k, v, causal=causal), rtol=0, atol=1e-12)
+
+
+def test_prefix_mean_and_scales_ignore_future_tiles():
+    """Centred prefix prologue: changing tokens of tile 2 and later leaves the
+    mean key and the codes and scales of tiles 0 and 1 untouched; with the
+    full-sequence mean the same change moves the mean and every K code's
+    centring."""
+    N = 512
+    q, k, v = operands(10, N)
+    kw = dict(center=True, tiles=True, prefix=True, rotate=True, signs=signs(64))
+    a = oracle.prepare(q, k, v, **kw)
+    q2, k2 = q.copy(), k.copy()
+    q2[:, :, 256:] *= np.float32(8.0)
+    k2[:, :, 300:] += np.float32(5.0)
+    b = oracle.prepare(q2, k2, v, **kw)
+    assert np.array_equal(a.k_mean, b.k_mean)
+    assert np.array_equal(a.q8[:, :, :256], b.q8[:, :, :256]) and np.array_equal(a.k8[:, :, :256], b.k8[:, :, :256])
+    assert np.array_equal(a.q_desc[..., :2], b.q_desc[..., :2]) and np.array_equal(a.k_desc[..., :2], b.k_desc[..., :2])
+    c = oracle.prepare(q, k, v, center=True, rotate=True, signs=signs(64))
+    e = oracle.prepare(q2, k2, v, center=True, rotate=True, signs=signs(64))
+    assert not np.array_equal(c.k_mean, e.k_mean)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_prefix_mean_output_close_to_ideal(order):
+    """The centred prefix prologue followed by the tile-scaled loop stays
+    within E4M3 noise of ideal attention on a shared-key workload."""
+    w = synth.illustration(N=384, d=64, shared_norm=30.0)
+    p = oracle.prepare(w.q, w.k, w.v, center=True, tiles=True, prefix=True, rotate=True, signs=w.signs)
+    out = oracle.attention_fp8(p, kv_order=order, block_n=64).out
+    ref = oracle.attention_f64(w.q, w.k, w.v, causal=True)
+    assert oracle.head_errors(out, ref).max() < 0.1
 
 
 def test_prefix_scales_ignore_future_tiles():
