@@ -92,8 +92,8 @@ size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* shape, uint32_t flags)
  * fp8_attn_prepare -- quantisation prologue.
  *
  * Computes, per (batch, head) over the full sequence (project page, second
- * section: independent Q/K/V scales over the full sequence for each batch and
- * head):
+ * section: one max-based scale per (batch, head) for each of Q, K and V, taken
+ * over all tokens):
  *   1. if CENTER: mu[b,g,:] = mean over all N tokens of K[b,g,:,:] (over the
  *      first min(N, 128) with PREFIX_SCALES), in binary64 (chunks of 64 tokens
  *      summed in order, chunk sums added in a pairwise tree), rounded to

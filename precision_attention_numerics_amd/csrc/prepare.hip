@@ -3,8 +3,9 @@
 // transposed layout the attention core reads.
 //
 // What is computed follows the attention-numerics project page (second
-// section: independent Q/K/V scales over the full sequence for each batch and
-// head; the same Hadamard on Q and K, never V; mean-key subtraction) and the
+// section: one max-based scale per (batch, head) for each of Q, K and V, taken
+// over all tokens; the same Hadamard on Q and K, never V; mean-key
+// subtraction) and the
 // study page ("See the vectors and the arithmetic": one maximum-based scale,
 // E4M3FN with round-to-nearest-even and saturation at +-448).
 //

@@ -56,8 +56,9 @@ def test_shared_key_vector_cancels(orc, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_mean_key_subtraction_preserves_attention(orc, causal):
-    """Subtracting the mean key preserves exact attention (project page, second
-    section; study page, mean subtraction before rotation)."""
+    """One vector subtracted from every key leaves binary64 softmax attention
+    unchanged (project page, second section; study page, mean subtraction
+    before rotation)."""
     q, k, v = rand((2, 4, 33, 16), 11), rand((2, 2, 33, 16), 12), rand((2, 2, 33, 16), 13)
     o1 = orc.attention_f64(q, k, v, causal=causal)
     o2 = orc.attention_f64(q, k - k.mean(axis=2, keepdims=True), v, causal=causal)
