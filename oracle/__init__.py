@@ -86,7 +86,7 @@ def _load():
     lib.orc_attention_fp8.argtypes = [_c_u8p, _c_u8p, _c_u8p, _c_f32p, _c_f32p, _c_f32p,
                                       _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
-                                      _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int]
+                                      _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int, _c_f64p]
     lib.orc_attention_fp8_tiles.argtypes = lib.orc_attention_fp8.argtypes
     lib.orc_attention_fp8_rowhash.argtypes = [_c_u8p, _c_u8p, _c_u8p, _c_f32p, _c_f32p, _c_f32p,
                                               _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
@@ -96,7 +96,8 @@ def _load():
     lib.orc_attention_pcast_f32.argtypes = [_c_f32p, _c_f32p, _c_f32p,
                                             _i64, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _i64,
-                                            _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int]
+                                            _c_f32p, _c_u8p, _c_u32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                            _c_f64p]
     _lib = lib
     return lib
 
@@ -265,6 +266,7 @@ class LoopResult:
     out: np.ndarray
     p: np.ndarray | None
     row_zeros: np.ndarray | None
+    lse: np.ndarray | None = None   # [B,Hq,nrows] binary64: (m*c + log2 l) * ln 2
 
 
 def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: float = 256.0,
@@ -288,14 +290,15 @@ def attention_fp8(prep: Prepared, softmax_scale: float | None = None, p_scale: f
     fn = _load().orc_attention_fp8_tiles if prep.tiles else _load().orc_attention_fp8
     if prep.int8:
         score_mode = "int8"
+    lse = np.empty((B, Hq, nrows), np.float64)
     rc = fn(_p(prep.q8, _c_u8p), _p(prep.k8, _c_u8p), _p(prep.v8, _c_u8p),
             _p(qd, _c_f32p), _p(kd, _c_f32p), _p(vd, _c_f32p),
             B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale), int(kv_order),
             int(block_n), int(causal), _p(r, _c_i32p), nrows, _p(out, _c_f32p),
             _p(p, _c_u8p), _p(z, _c_u32p), int(k_sink), SCORE_MODES[score_mode],
-            _threads(nthreads))
+            _threads(nthreads), _p(lse, _c_f64p))
     _check(rc, "attention_fp8")
-    return LoopResult(out, p, z)
+    return LoopResult(out, p, z, lse)
 
 
 def attention_fp8_rowhash(prep: Prepared, softmax_scale: float | None = None, p_scale: float = 256.0,
@@ -345,13 +348,14 @@ def attention_pcast_f32(q, k, v, softmax_scale: float | None = None, p_scale: fl
     out = np.empty((B, Hq, nrows, d), np.float32)
     p = np.empty((B, Hq, nrows, N), np.uint8) if want_p else None
     z = np.empty((B, Hq, nrows), np.uint32)
+    lse = np.empty((B, Hq, nrows), np.float64)
     rc = _load().orc_attention_pcast_f32(_p(q, _c_f32p), _p(k, _c_f32p), _p(v, _c_f32p),
                                          B, Hq, Hkv, N, d, float(softmax_scale), float(p_scale),
                                          int(kv_order), int(block_n), int(causal), _p(r, _c_i32p), nrows,
                                          _p(out, _c_f32p), _p(p, _c_u8p), _p(z, _c_u32p), int(k_sink),
-                                         int(p_cast), _threads(nthreads))
+                                         int(p_cast), _threads(nthreads), _p(lse, _c_f64p))
     _check(rc, "attention_pcast_f32")
-    return LoopResult(out, p, z)
+    return LoopResult(out, p, z, lse)
 
 
 # --------------------------------------------------------------- metrics

@@ -253,6 +253,7 @@ typedef struct {
   uint8_t* p_out;
   uint32_t* row_zeros;
   uint64_t* row_hash;
+  double* lse;         /* NULL or per row: natural-log sum-exp of the scaled logits */
   int32_t k_sink;
 } loop_args;
 
@@ -377,6 +378,9 @@ static void attn_row(void* p, int64_t item, double* scratch) {
   }
   if (a->row_zeros) a->row_zeros[bh * a->nrows + r] = zeros;
   if (a->row_hash) a->row_hash[bh * a->nrows + r] = hash;
+  /* sum_j exp(z_j) = 2^mc * l with z_j the scaled logits in natural units and
+   * mc the running max in base-2 units, so lse = (mc + log2 l) * ln 2 */
+  if (a->lse) a->lse[bh * a->nrows + r] = ((double)mc_prev + log2((double)l)) * 0.69314718055994530942;
 }
 
 static int check_loop(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float p_scale,
@@ -393,7 +397,7 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                       float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                       const int32_t* rows, int64_t nrows,
                       float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                      int score_mode, int nthreads) {
+                      int score_mode, int nthreads, double* lse) {
   if (!q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc || !out || d > 128) return -1;
   if (!rows) nrows = N;
   int rc = check_loop(B, Hq, Hkv, N, d, p_scale, kv_order, block_n, rows, nrows);
@@ -404,7 +408,7 @@ int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
   a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
   a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.rows = rows; a.out = out;
-  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
+  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink; a.lse = lse;
   return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
 }
 
@@ -435,7 +439,7 @@ int orc_attention_fp8_tiles(const uint8_t* q8, const uint8_t* k8, const uint8_t*
                             float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                             const int32_t* rows, int64_t nrows,
                             float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                            int score_mode, int nthreads) {
+                            int score_mode, int nthreads, double* lse) {
   if (!q8 || !k8 || !v8 || !q_desc || !k_desc || !v_desc || !out || d > 128) return -1;
   if (block_n <= 0 || ORC_TILE_TOKENS % block_n) return -1;
   if (!rows) nrows = N;
@@ -447,7 +451,7 @@ int orc_attention_fp8_tiles(const uint8_t* q8, const uint8_t* k8, const uint8_t*
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
   a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
   a.causal = causal; a.score_mode = score_mode; a.p_cast = 1; a.tiles = 1; a.rows = rows; a.out = out;
-  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
+  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink; a.lse = lse;
   return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
 }
 
@@ -456,7 +460,7 @@ int orc_attention_pcast_f32(const float* q, const float* k, const float* v,
                             float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                             const int32_t* rows, int64_t nrows,
                             float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                            int p_cast, int nthreads) {
+                            int p_cast, int nthreads, double* lse) {
   if (!q || !k || !v || !out) return -1;
   if (!rows) nrows = N;
   int rc = check_loop(B, Hq, Hkv, N, d, p_scale, kv_order, block_n, rows, nrows);
@@ -467,6 +471,6 @@ int orc_attention_pcast_f32(const float* q, const float* k, const float* v,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.nrows = nrows;
   a.softmax_scale = softmax_scale; a.p_scale = p_scale; a.kv_order = kv_order; a.block_n = block_n;
   a.causal = causal; a.p_cast = p_cast; a.rows = rows; a.out = out;
-  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink;
+  a.p_out = p_out; a.row_zeros = row_zeros; a.k_sink = k_sink; a.lse = lse;
   return orc_parallel_for(attn_row, &a, B * Hq * nrows, N + d, nthreads);
 }

@@ -84,14 +84,16 @@ int orc_prepare(const float* q, const float* k, const float* v,
                 uint8_t* q8, uint8_t* k8, uint8_t* v8,
                 float* q_desc, float* k_desc, float* v_desc, float* k_mean);
 
-/* Main-loop emulation on E4M3 codes. */
+/* Main-loop emulation on E4M3 codes.  lse (NULL or per row, binary64):
+ * (running max in base-2 scaled units + log2 l) * ln 2, the natural-log
+ * sum-exp of the scaled logits from the loop's own max and row sum. */
 int orc_attention_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                       const float* q_desc, const float* k_desc, const float* v_desc,
                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                       float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                       const int32_t* rows, int64_t nrows,
                       float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                      int score_mode, int nthreads);
+                      int score_mode, int nthreads, double* lse);
 
 /* The main loop of orc_attention_fp8 for its P~ codes only: per row the
  * checksum sum_j code_j * W_j mod 2^64 (W_j = splitmix64 output j+1 from seed
@@ -117,7 +119,7 @@ int orc_attention_fp8_tiles(const uint8_t* q8, const uint8_t* k8, const uint8_t*
                             float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                             const int32_t* rows, int64_t nrows,
                             float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                            int score_mode, int nthreads);
+                            int score_mode, int nthreads, double* lse);
 
 /* Main-loop emulation with binary32 Q/K/V (only P is cast). p_cast = 0
  * replaces the cast by the identity (structure checks). */
@@ -126,6 +128,6 @@ int orc_attention_pcast_f32(const float* q, const float* k, const float* v,
                             float softmax_scale, float p_scale, int kv_order, int block_n, int causal,
                             const int32_t* rows, int64_t nrows,
                             float* out, uint8_t* p_out, uint32_t* row_zeros, int32_t k_sink,
-                            int p_cast, int nthreads);
+                            int p_cast, int nthreads, double* lse);
 
 #endif

@@ -188,3 +188,27 @@ def test_score_matrix_model_symmetries(orc):
         vals = np.abs(orc.e4m3_decode(a).astype(np.float64) * orc.e4m3_decode(b))
         bound = sum(8 * vals[16 * i: 16 * i + 16].max() * 2.0 ** -12 for i in range(8)) + 16 * np.spacing(np.float32(abs(ex) + vals.sum()))
         assert abs(float(s) - ex) <= bound
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_lse_is_the_logsumexp_of_the_loop_logits(orc, order):
+    """The loop's LSE, (running max in base-2 units + log2 l) * ln 2, equals
+    the binary64 log-sum-exp of its own scaled logits s*c*ln 2 (scores from
+    the matrix-unit model) to binary32 rounding of l; and with binary32
+    operands and no cast, the log-sum-exp of the plain logits q.k/sqrt(d)."""
+    w = synth.illustration(N=96, d=64)
+    prep = orc.prepare(w.q, w.k, w.v, signs=w.signs, rotate=True)
+    res = orc.attention_fp8(prep, kv_order=order, block_n=64, causal=True)
+    ls2 = np.float32(np.float64(np.float32(1 / np.sqrt(64))) * 1.4426950408889634)
+    c = np.float64(np.float32(np.float32(prep.q_desc[0, 0]) * np.float32(prep.k_desc[0, 0])) * ls2)
+    for i in (0, 1, 37, 95):
+        s = np.array([float(orc.fp8_dot128(prep.q8[0, 0, i], prep.k8[0, 0, j])) for j in range(i + 1)])
+        z = s * c * np.log(2.0)
+        want = np.log(np.exp(z - z.max()).sum()) + z.max()
+        assert abs(res.lse[0, 0, i] - want) <= 1e-6 * max(1.0, abs(want)), (i, res.lse[0, 0, i], want)
+    q, k, v = rand32((1, 1, 80, 32), 3), rand32((1, 1, 80, 32), 4), rand32((1, 1, 80, 32), 5)
+    r = orc.attention_pcast_f32(q, k, v, causal=True, kv_order=order, block_n=16, p_cast=False)
+    z = (q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T) / np.sqrt(32)
+    z = np.where(np.tril(np.ones((80, 80), bool)), z, -np.inf)
+    want = np.log(np.exp(z - z.max(1, keepdims=True)).sum(1)) + z.max(1)
+    np.testing.assert_allclose(r.lse[0, 0], want, rtol=2e-6, atol=2e-6)
