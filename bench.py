@@ -10,7 +10,9 @@ One step = the whole hot path on resident inputs: fp8_attn_prepare (mean key,
 Hadamard, scales, E4M3 codes) + fp8_attn_fwd (online-softmax FP8 attention)
 + fp8_attn_head_error (per-head relative Frobenius error against the
 binary64 reference rows).  value = algorithmic FLOP of the causal forward
-(4*B*Hq*N^2*d/2) per step time.
+(4*B*Hq*N^2*d/2) per step time.  `detail` also carries the forward time of
+the Qwen2.5-0.5B and -1.5B shaped stacks (N = 1024, all layers x 3 texts in
+one launch).
 
 The CPU oracle (bit-faithful emulator and binary64 reference) runs on a
 bounded sample of query rows as the cpu_baseline leg; its reference rows feed
@@ -41,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qwen", action="store_true", help="skip the Qwen-shaped stacks' forward timing in detail")
+    ap.add_argument("--qwen-only", action="store_true",
+                    help="only time the Qwen-shaped stacks' forward (one JSON line of their detail; for profiling)")
     ap.add_argument("--tile-scales", action="store_true",
                     help="one Q/K scale per 128-token tile (the variant) instead of per (batch, head)")
     ap.add_argument("--int8-qk", action="store_true",
@@ -80,6 +85,13 @@ def profiled_traffic(kernel: str, summary: str = "attn_fwd_long_context_32k.json
     return None
 
 
+def kernel_name(args) -> str:
+    """The forward kernel the timed launch runs (as rocprofv3 names it)."""
+    if args.int8_qk:
+        return "k_attn_fwd<128, 128, 2, true, true, false, false, true>"
+    return "k_attn_fwd_pipe<true, true, %s>" % ("true" if args.tile_scales else "false")
+
+
 def sample_rows(N: int, tiles: int) -> np.ndarray:
     """First, middle and last 128-row query tiles (evenly spaced tiles when
     more are asked for)."""
@@ -87,6 +99,43 @@ def sample_rows(N: int, tiles: int) -> np.ndarray:
     idx = np.unique(np.linspace(0, nt - 1, tiles).round().astype(int))
     rows = np.concatenate([np.arange(t * 128, min(N, t * 128 + 128)) for t in idx])
     return rows.astype(np.int32)
+
+
+def qwen_stacks(pan, synth, torch, args) -> dict:
+    """Forward of the Qwen2.5-0.5B and -1.5B shaped stacks (all layers x 3 texts
+    as one batch, N = 1024, centred and rotated, S = 256, reverse, block 128):
+    mean HIP-event time of the forward launch on the current stream."""
+    out = {}
+    for name, gen in (("qwen2.5-0.5b_stack", synth.qwen05b), ("qwen2.5-1.5b_stack", synth.qwen15b)):
+        t0 = time.time()
+        w = gen()
+        B, hq, N, d = w.q.shape
+        hkv = w.k.shape[1]
+        pipe = pan.AttnPipeline(B, hq, hkv, N, d)
+        q = torch.from_numpy(w.q).cuda().to(torch.bfloat16)
+        k = torch.from_numpy(w.k).cuda().to(torch.bfloat16)
+        v = torch.from_numpy(w.v).cuda().to(torch.bfloat16)
+        signs = torch.from_numpy(w.signs).cuda()
+        prep = pipe.prepare(q, k, v, rotate=True, center=True, signs=signs)
+        o = torch.empty((B, hq, N, d), dtype=torch.float32, device="cuda")
+        for _ in range(args.warmup):
+            pipe.fwd(prep, p_scale=256.0, kv_order=1, block_n=128, causal=True, out=o)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            pipe.fwd(prep, p_scale=256.0, kv_order=1, block_n=128, causal=True, out=o)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        flop = 4.0 * B * hq * N * N * d / 2.0
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"shape": f"B={B} (layers x 3 texts) Hq={hq} Hkv={hkv} N={N} d={d}", "fwd_ms": ms,
+                     "fwd_tflops": tf, "fwd_frac_of_fp8_peak": tf / FP8_DENSE_PEAK_TFLOPS}
+        print(f"[bench] {name}: {out[name]} (inputs {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+        del q, k, v, prep, o
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -106,6 +155,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
+    if args.qwen_only:
+        print(json.dumps({"detail": qwen_stacks(pan, synth, torch, args)}), flush=True)
+        return
     t0 = time.time()
     w = synth.long_context(N=args.seqlen)
     B, hq, N, d = w.q.shape
@@ -128,26 +180,29 @@ def main():
         import oracle
         threads = oracle._threads(None)
         pairs = float(B * hq * np.sum(rows + 1))                      # visible (query, key) pairs of the sample
-        t_emu = 0.0
+        t_loop = t_prep = 0.0
         for cond in ("centered_rotated", "rotated"):
             fl = synth.CONDITIONS[cond]
             ta = time.perf_counter()
             op = oracle.prepare(w.q, w.k, w.v, signs=w.signs, tiles=args.tile_scales, int8=args.int8_qk, **fl)
+            tm = time.perf_counter()
             emu = oracle.attention_fp8(op, p_scale=256.0, kv_order=1, block_n=128, causal=True, rows=rows)
             tb = time.perf_counter()
             if cond == "centered_rotated":
-                t_emu = tb - ta
+                t_prep, t_loop = tm - ta, tb - tm
             emu_rows[cond] = emu.out
-            print(f"[bench] oracle emulator {cond}: {tb - ta:.1f}s", file=sys.stderr, flush=True)
+            print(f"[bench] oracle emulator {cond}: prologue {tm - ta:.1f}s, main loop {tb - tm:.1f}s",
+                  file=sys.stderr, flush=True)
         ta = time.perf_counter()
         ideal = oracle.attention_f64(w.q, w.k, w.v, causal=True, rows=rows)
         t_ideal = time.perf_counter() - ta
         ref_rows["f64"] = ideal
         print(f"[bench] oracle binary64 reference: {t_ideal:.1f}s", file=sys.stderr, flush=True)
-        cpu = {"value": 4.0 * d * pairs / t_emu / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": (f"bit-faithful emulator (prologue on all {N} tokens + main loop on {rows.size} query rows "
-                          f"x {hq} heads = first/middle/last 128-row tiles), centered_rotated; {t_emu:.1f}s; "
-                          f"binary64 reference on the same rows {t_ideal:.1f}s")}
+        cpu = {"value": 4.0 * d * pairs / t_loop / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": (f"bit-faithful emulator main loop on {rows.size} query rows x {hq} heads (first/middle/last "
+                          f"128-row tiles: {pairs:.3g} visible query-key pairs), centered_rotated: {t_loop:.1f}s; "
+                          f"value = 4*d FLOP per pair over that time.  Not in value: the emulated prologue on all "
+                          f"{N} tokens ({t_prep:.1f}s) and the binary64 reference on the same rows ({t_ideal:.1f}s)")}
 
     ref = torch.from_numpy(ref_rows["f64"]).cuda() if ref_rows else torch.zeros((B, hq, rows.size, d), dtype=torch.float64, device="cuda")
     prep = pipe.alloc_prepared(args.tile_scales, args.int8_qk)
@@ -204,6 +259,9 @@ def main():
         results[cond] = res
         print(f"[bench] {cond}: {res}", file=sys.stderr, flush=True)
 
+    if not args.no_qwen:
+        results.update(qwen_stacks(pan, synth, torch, args))
+
     main_res = results["centered_rotated"]
     fwd_tflops = flop / (main_res["fwd_ms"] * 1e-3) / 1e12
     value = flop / (main_res["ms_per_step"] * 1e-3) / 1e12
@@ -228,14 +286,11 @@ def main():
                    "pct_of_fp8_peak": round(100 * value / FP8_DENSE_PEAK_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
-                     "traffic": profiled_traffic(
-                         "k_attn_fwd<128, 128, 2, true, true, false, %s, %s>" % (
-                             "true" if args.tile_scales else "false", "true" if args.int8_qk else "false"),
+                     "traffic": profiled_traffic(kernel_name(args),
                          ("attn_fwd_tile_scaled_long_context_32k.json" if args.tile_scales else
                           "attn_fwd_int8qk_long_context_32k.json" if args.int8_qk else
                           "attn_fwd_long_context_32k.json")),
-                     "kernel": "k_attn_fwd<128,128,2,causal,pow2%s%s>" % (",tiles" if args.tile_scales else "",
-                                                                         ",int8qk" if args.int8_qk else ""),
+                     "kernel": kernel_name(args),
                      "flop_per_launch": flop},
         "cpu_baseline": cpu,
         "detail": results,

@@ -7,10 +7,10 @@ sha256 of the kernel source they were measured on)
 
 PROFDIR holds the sub-directories written by these commands (run from /tmp,
 TMPDIR=/tmp, R = repository root):
-  trace: rocprofv3 --kernel-trace --stats -S --output-format csv -d PROFDIR/trace -o trace -- python3 R/bench.py --no-cpu-baseline --steps 20 --warmup 5
-  fetch: rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROFDIR/fetch -o fetch -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
-  write: rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROFDIR/write -o write -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
-  sq:    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE --output-format csv -d PROFDIR/sq -o sq -- python3 R/bench.py --no-cpu-baseline --steps 2 --warmup 0
+  trace: rocprofv3 --kernel-trace --stats -S --output-format csv -d PROFDIR/trace -o trace -- python3 R/bench.py --no-cpu-baseline --no-qwen --steps 20 --warmup 5
+  fetch: rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROFDIR/fetch -o fetch -- python3 R/bench.py --no-cpu-baseline --no-qwen --steps 2 --warmup 0
+  write: rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROFDIR/write -o write -- python3 R/bench.py --no-cpu-baseline --no-qwen --steps 2 --warmup 0
+  sq:    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE --output-format csv -d PROFDIR/sq -o sq -- python3 R/bench.py --no-cpu-baseline --no-qwen --steps 2 --warmup 0
   copyf: rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROFDIR/copyf -o copyf -- python3 R/bench.py --copy-calibration-mib 1024 --steps 3
   copyw: rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROFDIR/copyw -o copyw -- python3 R/bench.py --copy-calibration-mib 1024 --steps 3
 """
