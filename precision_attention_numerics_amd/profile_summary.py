@@ -27,7 +27,7 @@ COPY_BYTES = 1024 * (1 << 20)
 
 
 def short(name: str) -> str:
-    name = name.replace("void ", "").replace("fp8a::", "")
+    name = name.replace("void ", "").replace("fp8a::", "").replace("(anonymous namespace)::", "")
     return name.split("(")[0]
 
 
