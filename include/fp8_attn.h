@@ -7,7 +7,9 @@
  *   - Every pointer argument named as "device" is device memory owned by the
  *     caller; its lifetime must cover the work enqueued on `stream`.  The
  *     library allocates and frees nothing; scratch memory comes from the
- *     caller through a workspace argument sized by the *_workspace_bytes call.
+ *     caller through a workspace argument sized by the *_workspace_bytes call,
+ *     except for fp8_attn_prepare_noalloc, which uses a fixed device array of
+ *     the library (FP8A_NOALLOC_SCRATCH_BYTES on every GPU it runs on).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call validates its arguments on the host first; a failed check
  *     returns a negative status and enqueues nothing.  No call synchronises.
@@ -17,8 +19,9 @@
  *     head h reads KV head h / (hq / hkv).
  *   - Quantised operands use a padded token count Np = fp8_attn_padded_seqlen(N)
  *     (a multiple of 128); rows/columns past N hold code 0.
- *   - Thread safety: no global mutable state; concurrent calls on different
- *     streams with disjoint outputs are independent.
+ *   - Thread safety: concurrent calls on different streams with disjoint
+ *     outputs are independent, except fp8_attn_prepare_noalloc calls that
+ *     overlap on one GPU (they share that GPU's scratch array and race).
  */
 #ifndef FP8_ATTN_H
 #define FP8_ATTN_H
@@ -129,6 +132,31 @@ int fp8_attn_prepare(const fp8a_shape* shape, fp8a_dtype in_dtype,
                      uint8_t* q8, uint8_t* k8, uint8_t* v8t,
                      float* q_desc, float* k_desc, float* v_desc, float* k_mean,
                      int32_t* status_word, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_attn_prepare_noalloc -- fp8_attn_prepare without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments (minus workspace), results and errors as fp8_attn_prepare; its
+ * scratch is a static device array of FP8A_NOALLOC_SCRATCH_BYTES per GPU that
+ * the library holds until the process ends.  The call allocates nothing.
+ *
+ *   - FP8A_ERR_WORKSPACE when fp8_attn_prepare_workspace_bytes(shape, flags)
+ *     exceeds FP8A_NOALLOC_SCRATCH_BYTES (8 MiB: with CENTER_K, d = 128 and
+ *     8 KV heads, up to 32768 tokens); FP8A_ERR_HIP when the array's device
+ *     address cannot be looked up (done once per device, on the first call
+ *     made with that device current).
+ *   - Every call on a GPU uses the same array; the call clears what must
+ *     start at zero.  Calls that overlap on one GPU (several streams or host
+ *     threads) race on it and give unspecified results: serialise them.
+ */
+#define FP8A_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fp8_attn_prepare_noalloc(const fp8a_shape* shape, fp8a_dtype in_dtype,
+                             const void* q, const void* k, const void* v, uint32_t flags,
+                             const int8_t* rot_signs,
+                             uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                             float* q_desc, float* k_desc, float* v_desc, float* k_mean,
+                             int32_t* status_word, void* stream);
 
 /*
  * fp8_attn_fwd -- attention main loop and epilogue.

@@ -49,6 +49,8 @@ def _load():
     lib.fp8_attn_prepare_workspace_bytes.restype = sz
     lib.fp8_attn_prepare.argtypes = [sp, ctypes.c_int, vp, vp, vp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fp8_attn_prepare.restype = ctypes.c_int
+    lib.fp8_attn_prepare_noalloc.argtypes = [sp, ctypes.c_int, vp, vp, vp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp8_attn_prepare_noalloc.restype = ctypes.c_int
     lib.fp8_attn_fwd.argtypes = [sp, ctypes.c_int, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, vp, vp, vp, vp, vp,
                                  i32, vp]
     lib.fp8_attn_fwd.restype = ctypes.c_int
@@ -123,6 +125,18 @@ def fp8_attn_prepare(shape: Shape, q, k, v, flags: int, rot_signs, q8, k8, v8t, 
                                _stream(stream))
     if rc != 0:
         raise Fp8AttnError(rc, "fp8_attn_prepare")
+
+
+def fp8_attn_prepare_noalloc(shape: Shape, q, k, v, flags: int, rot_signs, q8, k8, v8t, q_desc, k_desc, v_desc,
+                             k_mean=None, status_word=None, stream=None) -> None:
+    rc = _lib.fp8_attn_prepare_noalloc(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), int(flags),
+                                       _ptr(rot_signs), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_desc), _ptr(k_desc),
+                                       _ptr(v_desc), _ptr(k_mean), _ptr(status_word), _stream(stream))
+    if rc != 0:
+        raise Fp8AttnError(rc, "fp8_attn_prepare_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def fp8_attn_fwd(shape: Shape, qkv_dtype: int, q, k, v, q_desc, k_desc, v_desc, softmax_scale: float,

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fp8_attn.h"
 #include "attn.hpp"
 #include "prepare.hpp"
@@ -85,16 +87,33 @@ bool p_scale_setup(float S, bool* pow2, float* inv_S, uint32_t* bad0, uint32_t* 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8A_OK : FP8A_ERR_HIP; }
 
-}  // namespace
+// Workspace of fp8_attn_prepare_noalloc: one copy in every GPU's memory, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address looked up once per device below.
+constexpr size_t kNoAllocScratch = FP8A_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratch];
 
-extern "C" {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
 
-int32_t fp8_attn_padded_seqlen(int32_t seqlen) {
-  if (seqlen < 1 || seqlen > (1 << 30)) return 0;
-  return (seqlen + 127) / 128 * 128;
+// The device address of the current device's scratch, looked up on the first
+// call made on that device.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8A_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FP8A_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP8A_OK;
 }
 
-size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* s, uint32_t flags) {
+size_t prepare_ws_bytes(const fp8a_shape* s, uint32_t flags) {
   if (check_shape(s) != FP8A_OK) return 0;
   const size_t B = s->batch, hq = s->hq, hkv = s->hkv, d = s->head_dim;
   const size_t nt = (flags & FP8A_TILE_SCALES) ? static_cast<size_t>(fp8_attn_padded_seqlen(s->seqlen)) / 128 : 1;
@@ -106,10 +125,12 @@ size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* s, uint32_t flags) {
   return bytes;
 }
 
-int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, const void* k, const void* v,
-                     uint32_t flags, const int8_t* rot_signs, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
-                     float* q_desc, float* k_desc, float* v_desc, float* k_mean, int32_t* status_word,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+// fp8_attn_prepare with the workspace given; with noalloc the workspace is
+// the current device's scratch (looked up once all arguments have passed).
+int prepare_common(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, const void* k, const void* v,
+                   uint32_t flags, const int8_t* rot_signs, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                   float* q_desc, float* k_desc, float* v_desc, float* k_mean, int32_t* status_word,
+                   void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (in_dtype != FP8A_F32 && in_dtype != FP8A_BF16) return FP8A_ERR_UNSUPPORTED;
@@ -121,7 +142,12 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
   if ((flags & FP8A_ROTATE_QK) && !rot_signs) return FP8A_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t))
     return FP8A_ERR_SHAPE;
-  const size_t need = fp8_attn_prepare_workspace_bytes(s, flags);
+  const size_t need = prepare_ws_bytes(s, flags);
+  if (noalloc) {
+    if (need > kNoAllocScratch) return FP8A_ERR_WORKSPACE;
+    if ((rc = device_scratch(&workspace))) return rc;
+    workspace_bytes = kNoAllocScratch;
+  }
   if (!workspace || workspace_bytes < need) return FP8A_ERR_WORKSPACE;
   fp8a::PrepareArgs a;
   memset(&a, 0, sizeof a);
@@ -155,6 +181,33 @@ int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, co
     a.k_mean = k_mean ? k_mean : reinterpret_cast<float*>(ws);
   }
   return hip_status(fp8a::launch_prepare(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp8_attn_padded_seqlen(int32_t seqlen) {
+  if (seqlen < 1 || seqlen > (1 << 30)) return 0;
+  return (seqlen + 127) / 128 * 128;
+}
+
+size_t fp8_attn_prepare_workspace_bytes(const fp8a_shape* s, uint32_t flags) { return prepare_ws_bytes(s, flags); }
+
+int fp8_attn_prepare(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, const void* k, const void* v,
+                     uint32_t flags, const int8_t* rot_signs, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                     float* q_desc, float* k_desc, float* v_desc, float* k_mean, int32_t* status_word,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prepare_common(s, in_dtype, q, k, v, flags, rot_signs, q8, k8, v8t, q_desc, k_desc, v_desc, k_mean,
+                        status_word, workspace, workspace_bytes, stream, false);
+}
+
+int fp8_attn_prepare_noalloc(const fp8a_shape* s, fp8a_dtype in_dtype, const void* q, const void* k,
+                             const void* v, uint32_t flags, const int8_t* rot_signs, uint8_t* q8, uint8_t* k8,
+                             uint8_t* v8t, float* q_desc, float* k_desc, float* v_desc, float* k_mean,
+                             int32_t* status_word, void* stream) {
+  return prepare_common(s, in_dtype, q, k, v, flags, rot_signs, q8, k8, v8t, q_desc, k_desc, v_desc, k_mean,
+                        status_word, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

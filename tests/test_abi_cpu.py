@@ -122,6 +122,35 @@ def test_prepare_rejects(abi):
                                      None, None, FAKE, 1 << 30, None) == -1
 
 
+def test_prepare_noalloc_rejects(abi):
+    """The no-alloc prologue validates like fp8_attn_prepare and refuses a
+    shape whose workspace exceeds its fixed scratch, before any HIP call."""
+    _no_gpu()
+    f = abi._lib.fp8_attn_prepare_noalloc
+
+    def call(shape, flags=0, q=FAKE, signs=FAKE):
+        return f(ctypes.byref(shape), 1, q, FAKE, FAKE, flags, signs, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                 None, None)
+    big = abi.make_shape(1, 32, 8, 65536, 128)
+    cen = abi.FP8A_ROTATE_QK | abi.FP8A_CENTER_K
+    assert abi.prepare_workspace_bytes(big, cen) > abi.NOALLOC_SCRATCH_BYTES
+    assert call(big, cen) == -5
+    long_ctx = abi.make_shape(1, 32, 8, 32768, 128)                  # the 32k workload fits
+    assert abi.prepare_workspace_bytes(long_ctx, cen) <= abi.NOALLOC_SCRATCH_BYTES
+    assert abi.prepare_workspace_bytes(long_ctx, cen | abi.FP8A_TILE_SCALES) <= abi.NOALLOC_SCRATCH_BYTES
+    assert call(abi.make_shape(1, 2, 1, 64, 96)) == -2
+    assert call(abi.make_shape(1, 2, 1, 64, 64), flags=abi.FP8A_PREFIX_SCALES) == -4
+    assert call(abi.make_shape(1, 2, 1, 64, 64), q=None) == -1
+    assert call(abi.make_shape(1, 2, 1, 64, 64), flags=abi.FP8A_ROTATE_QK, signs=None) == -1
+    assert f(None, 1, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+
+
+def test_noalloc_scratch_size_matches_the_header(abi):
+    text = open(abi.HEADER).read()
+    assert "#define FP8A_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)" in text
+    assert abi.NOALLOC_SCRATCH_BYTES == 8 << 20
+
+
 def test_fwd_rejects(abi):
     _no_gpu()
     ok = abi.make_shape(1, 2, 1, 64, 64)
