@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 #pragma unroll
       for (int ct = 0; ct < D / 16; ++ct) {
         const v4f o = oacc[qt][ct] * f;
-        *reinterpret_cast<float4*>(orow + 16 * ct + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+        store4_stream(orow + 16 * ct + 4 * lg, o[0], o[1], o[2], o[3]);
       }
       if (p.lse && lg == 0) p.lse[static_cast<int64_t>(bh) * N + i] = (mcp[qt] + __log2f(l)) * 0.69314718055994531f;
     }
@@ -617,7 +617,7 @@ __device__ __forceinline__ void store_tile(const Tile& X, const FwdParams& p, in
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) {
       const v4f o = X.o[ct] * f;
-      *reinterpret_cast<float4*>(orow + 16 * ct + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
+      store4_stream(orow + 16 * ct + 4 * lg, o[0], o[1], o[2], o[3]);
     }
     if (p.lse && lg == 0) p.lse[static_cast<int64_t>(bh) * N + i] = (X.mcp + __log2f(l)) * 0.69314718055994531f;
   }

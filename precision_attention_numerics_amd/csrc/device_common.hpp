@@ -7,6 +7,14 @@ namespace fp8a {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Output rows are written once and never read back by the kernel: streaming
+// (non-temporal) stores keep them from displacing K/V lines in the caches.
+// Used where a wave's store covers 64 contiguous bytes of a row; with 32-byte
+// pieces (the head_dim 64 kernel) they measured slower than plain stores.
+__device__ __forceinline__ void store4_stream(float* dst, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(v4f{a, b, c, d}, reinterpret_cast<v4f*>(dst));
+}
 typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
