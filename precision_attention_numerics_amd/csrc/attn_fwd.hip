@@ -87,10 +87,10 @@ __device__ __forceinline__ int key_of_row(int r) {
 // are fixed per (wave, e) and computed once (fill_offsets); each block adds a
 // uniform base (fill_issue).  The offset arrays are the kernel's locals
 // (KI and VI entries); after inlining they stay in registers.
-template <int D, int BC>
+template <int D, int BC, int WAVES = kWaves>
 __device__ __forceinline__ void fill_offsets(int wv, int lane, int Np, uint32_t* koff, uint32_t* voff) {
   constexpr int UK = D / 16, UV = BC / 16;
-  constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
+  constexpr int KI = BC * UK / 64 / WAVES, VI = D * UV / 64 / WAVES;
 #pragma unroll
   for (int e = 0; e < KI; ++e) {
     const int u = 64 * (wv * KI + e) + lane;
@@ -548,22 +548,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(const FwdParams p) {
 namespace pipe {
 
 constexpr int D = 128, BC = 128, T = 8, UK = 8, UV = 8, KBYTES = BC * D;
-constexpr int KI = BC * UK / 64 / kWaves, VI = D * UV / 64 / kWaves;
+// DMA instructions per wave for one K or V^T tile, with W waves per workgroup
+template <int W>
+constexpr int KI = BC * UK / 64 / W;
+template <int W>
+constexpr int VI = D * UV / 64 / W;
 
+template <int W>
 __device__ __forceinline__ void fill_k(const __amdgpu_buffer_rsrc_t krs, int blk, int wv, const uint32_t* koff,
                                        uint8_t* kbuf) {
   const uint32_t kblk = static_cast<uint32_t>(blk) * (BC * D);
 #pragma unroll
-  for (int e = 0; e < KI; ++e)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI + e)), 16, koff[e], kblk, 0, 0);
+  for (int e = 0; e < KI<W>; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(kbuf + 1024 * (wv * KI<W> + e)), 16, koff[e], kblk, 0,
+                                             0);
 }
 
+template <int W>
 __device__ __forceinline__ void fill_v(const __amdgpu_buffer_rsrc_t vrs, int blk, int wv, const uint32_t* voff,
                                        uint8_t* vbuf) {
   const uint32_t vblk = static_cast<uint32_t>(blk) * BC;
 #pragma unroll
-  for (int e = 0; e < VI; ++e)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * (wv * VI + e)), 16, voff[e], vblk, 0, 0);
+  for (int e = 0; e < VI<W>; ++e)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(vbuf + 1024 * (wv * VI<W> + e)), 16, voff[e], vblk, 0,
+                                             0);
 }
 
 // S^T of one query tile for the block in kt: eight 16-key MFMA tiles.
@@ -800,9 +808,15 @@ __device__ __attribute__((always_inline)) inline void back_step(float (&part)[T]
 
 }  // namespace pipe
 
-template <bool CAUSAL, bool POW2, bool TILES>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p) {
+// NT query tiles of 16 rows per wave and W = 8 / NT waves: a workgroup covers
+// one 128-row query tile either way.  With NT = 2 two waves share a SIMD (256
+// registers each) and each K/V operand read from LDS feeds two matrix
+// instructions; with NT = 1 four waves share a SIMD (128 registers each), so
+// more waves interleave their vector work, for twice the LDS reads per row.
+template <bool CAUSAL, bool POW2, bool TILES, int NT>
+__global__ __launch_bounds__(64 * 8 / NT, 4 / NT) void k_attn_fwd_pipe(const FwdParams p) {
   using namespace pipe;
+  constexpr int W = 8 / NT;
   constexpr int QROWS = 128;
   constexpr int KPL = BC / 4;
   __shared__ __align__(16) uint8_t klds[2 * KBYTES];
@@ -834,11 +848,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
 
   const int tid = threadIdx.x, lane = tid % kWave, wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n16 = lane & 15, lg = lane >> 4;
-  const int wrow0 = q0 + wv * 32;
+  const int wrow0 = q0 + wv * 16 * NT;
 
-  Tile A, B;
-  init_tile(A, p.q8, bh, Np, wrow0 + n16, lg);
-  init_tile(B, p.q8, bh, Np, wrow0 + 16 + n16, lg);
+  Tile X[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) init_tile(X[k], p.q8, bh, Np, wrow0 + 16 * k + n16, lg);
   const int kofs0 = 16 * (n16 * UK + ((2 * lg) ^ swz<UK>(n16)));
   const int kofs1 = 16 * (n16 * UK + ((2 * lg + 1) ^ swz<UK>(n16)));
   const int vofs0 = 16 * (n16 * UV + ((2 * lg) ^ swz<UV>(n16)));
@@ -849,8 +863,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
   const uint32_t head_bytes = static_cast<uint32_t>(Np) * D;
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(p.k8 + static_cast<int64_t>(bg) * Np * D, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(p.v8t + static_cast<int64_t>(bg) * D * Np, head_bytes);
-  uint32_t koff[KI], voff[VI];
-  fill_offsets<D, BC>(wv, lane, Np, koff, voff);
+  uint32_t koff[KI<W>], voff[VI<W>];
+  fill_offsets<D, BC, W>(wv, lane, Np, koff, voff);
 
   // block visited at step it, its logit factor and whether the wave must mask it
   auto blk_of = [&](int it) { return p.kv_order ? J - it : it; };
@@ -882,28 +896,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
     });
   };
   auto front_first = [&](int blk) __attribute__((always_inline)) {
-    Front fa, fb;
+    Front f[NT];
     if (masked(blk)) {
-      front_all(A, fa, blk, yes{});
-      front_all(B, fb, blk, yes{});
+#pragma unroll
+      for (int k = 0; k < NT; ++k) front_all(X[k], f[k], blk, yes{});
     } else {
-      front_all(A, fa, blk, no{});
-      front_all(B, fb, blk, no{});
+#pragma unroll
+      for (int k = 0; k < NT; ++k) front_all(X[k], f[k], blk, no{});
     }
   };
 
   // ---- first block: K tile, Q.K^T of both tiles (one K read serves both),
   // the front of both softmaxes
-  fill_k(krs, blk_of(0), wv, koff, klds);
+  fill_k<W>(krs, blk_of(0), wv, koff, klds);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
-  if (J >= 1) fill_k(krs, blk_of(1), wv, koff, klds + KBYTES);
-  fill_v(vrs, blk_of(0), wv, voff, vlds);
+  if (J >= 1) fill_k<W>(krs, blk_of(1), wv, koff, klds + KBYTES);
+  fill_v<W>(vrs, blk_of(0), wv, voff, vlds);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const v8i a = lds_read_pair(klds + kofs0 + t * 256 * UK, klds + kofs1 + t * 256 * UK);
-    A.s[t] = mfma_f8(a, A.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-    B.s[t] = mfma_f8(a, B.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+    for (int k = 0; k < NT; ++k) X[k].s[t] = mfma_f8(a, X[k].q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
   }
   front_first(blk_of(0));
 
@@ -918,11 +932,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
     // after the barrier), and every wave is done with the buffers refilled here
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (it + 2 <= J) fill_k(krs, blk_of(it + 2), wv, koff, klds + (it & 1) * KBYTES);
-    fill_v(vrs, blk_of(it + 1), wv, voff, vlds + ((it + 1) & 1) * KBYTES);
+    if (it + 2 <= J) fill_k<W>(krs, blk_of(it + 2), wv, koff, klds + (it & 1) * KBYTES);
+    fill_v<W>(vrs, blk_of(it + 1), wv, voff, vlds + ((it + 1) & 1) * KBYTES);
     // O by block it's alpha before its P.V below (the previous P.V has completed)
-    rescale_o_if_moved(A);
-    rescale_o_if_moved(B);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) rescale_o_if_moved(X[k]);
     const uint8_t* kt = klds + ((it + 1) & 1) * KBYTES;
     const uint8_t* vt = vlds + (it & 1) * KBYTES;
     const int bn = blk_of(it + 1);
@@ -941,8 +955,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
       else return lds_read_pair(vt + vofs0 + (n - 8) * 256 * UV, vt + vofs1 + (n - 8) * 256 * UV);
     };
     v8i ops[3];
-    Front fa, fb;
-    float pa[T], pb[T];
+    Front f[NT];
+    float part[NT][T];
     ops[0] = read_op(std::integral_constant<int, 0>{});
     ops[1] = read_op(std::integral_constant<int, 1>{});
     static_for<0, 16>([&](auto nc) __attribute__((always_inline)) {
@@ -950,22 +964,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
       constexpr int j = n % 8;
       if constexpr (n + 2 < 16) ops[(n + 2) % 3] = read_op(std::integral_constant<int, n + 2>{});
       if constexpr (n < 8) {
-        back_step<j, MB, POW2>(pa, A, p);
-        back_step<j, MB, POW2>(pb, B, p);
-        A.s[j] = mfma_f8(ops[n % 3], A.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-        B.s[j] = mfma_f8(ops[n % 3], B.q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int k = 0; k < NT; ++k) back_step<j, MB, POW2>(part[k], X[k], p);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) X[k].s[j] = mfma_f8(ops[n % 3], X[k].q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
       } else {
-        A.o[j] = mfma_f8(ops[n % 3], A.pop, A.o[j]);
-        B.o[j] = mfma_f8(ops[n % 3], B.pop, B.o[j]);
-        front_step<j, MF, CAUSAL, TILES, false>(fa, A, cn, jbn, N, p);
-        front_step<j, MF, CAUSAL, TILES, false>(fb, B, cn, jbn, N, p);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) X[k].o[j] = mfma_f8(ops[n % 3], X[k].pop, X[k].o[j]);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) front_step<j, MF, CAUSAL, TILES, false>(f[k], X[k], cn, jbn, N, p);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    A.alpha = fa.alpha;
-    B.alpha = fb.alpha;
-    if (fa.gate) softmax_screen<T>(A.s, p);
-    if (fb.gate) softmax_screen<T>(B.s, p);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) X[k].alpha = f[k].alpha;
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+      if (f[k].gate) softmax_screen<T>(X[k].s, p);
   };
   const bool first_masked = masked(blk_of(0));
   const bool last_masked = J >= 1 && masked(blk_of(J));
@@ -982,27 +997,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd_pipe(const FwdParams p
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (masked(blk_of(J))) {
-    back_all(A, yes{});
-    back_all(B, yes{});
+#pragma unroll
+    for (int k = 0; k < NT; ++k) back_all(X[k], yes{});
   } else {
-    back_all(A, no{});
-    back_all(B, no{});
+#pragma unroll
+    for (int k = 0; k < NT; ++k) back_all(X[k], no{});
   }
   {
     const uint8_t* vt = vlds + (J & 1) * KBYTES;
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct) {
       const v8i a = lds_read_pair(vt + vofs0 + ct * 256 * UV, vt + vofs1 + ct * 256 * UV);
-      rescale_o(A, ct);
-      rescale_o(B, ct);
-      A.o[ct] = mfma_f8(a, A.pop, A.o[ct]);
-      B.o[ct] = mfma_f8(a, B.pop, B.o[ct]);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) rescale_o(X[k], ct);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) X[k].o[ct] = mfma_f8(a, X[k].pop, X[k].o[ct]);
     }
   }
 
   // ---- epilogue
-  store_tile(A, p, bh, N, vdesc, lg);
-  store_tile(B, p, bh, N, vdesc, lg);
+#pragma unroll
+  for (int k = 0; k < NT; ++k) store_tile(X[k], p, bh, N, vdesc, lg);
 }
 
 // -------------------------------------------------------- P-cast-only path
@@ -1078,13 +1093,20 @@ __global__ __launch_bounds__(64) void k_attn_pcast_f32(const PcastParams p) {
 
 // ------------------------------------------------------------------ launch
 
+// Query tiles per wave of the pipelined kernel: two (two waves per SIMD).  One
+// tile per wave (four waves per SIMD, 128 registers each) passes the same
+// parity tests but measured 4% slower on the 32k workload: the doubled LDS
+// operand reads and per-step work per row outweigh the extra waves.
+constexpr int kPipeTiles = 2;
+
 template <int D, int BC, bool CAUSAL, bool POW2, bool DUMP>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.B * p.hq * p.n_qtiles));
   if constexpr (D == 128 && BC == 128 && !DUMP) {
     if (!p.int8 && !p.no_pipe) {
-      if (p.tiles) k_attn_fwd_pipe<CAUSAL, POW2, true><<<grid, dim3(kThreads), 0, st>>>(p);
-      else k_attn_fwd_pipe<CAUSAL, POW2, false><<<grid, dim3(kThreads), 0, st>>>(p);
+      constexpr int NT = kPipeTiles;
+      if (p.tiles) k_attn_fwd_pipe<CAUSAL, POW2, true, NT><<<grid, dim3(64 * 8 / NT), 0, st>>>(p);
+      else k_attn_fwd_pipe<CAUSAL, POW2, false, NT><<<grid, dim3(64 * 8 / NT), 0, st>>>(p);
       return hipGetLastError();
     }
   }
