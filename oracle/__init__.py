@@ -43,7 +43,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FP8A_ORACLE_LIB selects another build of the same sources (the sanitizer
+# build, oracle/build.py --sanitize)
+_LIB_PATH = os.environ.get("FP8A_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 ROTATE = 1

@@ -14,7 +14,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfp8attn.so")
+# FP8A_LIB selects another build of the same sources (the host-sanitizer
+# build, build.py --sanitize)
+LIB_PATH = os.environ.get("FP8A_LIB") or os.path.join(_HERE, "libfp8attn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8_attn.h")
 
 FP8A_F32, FP8A_BF16, FP8A_F64, FP8A_E4M3, FP8A_I8QK = 0, 1, 2, 3, 4

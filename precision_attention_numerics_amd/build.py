@@ -29,6 +29,25 @@ COMPILE_FLAGS = [
 # a symbol left undefined (e.g. a kernel launch stub the host pass did not
 # emit) fails the build instead of the first load
 LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined"]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the entry
+# points (argument validation, workspace layout, launch set-up): abi.hip is
+# recompiled with the sanitizers on its host pass only (device code is never
+# instrumented) and linked with the other objects into SAN_LIB, which needs
+# the clang sanitizer runtime preloaded (SAN_RUNTIME).
+SAN_LIB = os.path.join(HERE, "libfp8attn_san.so")
+SAN_HOST_FLAGS = []
+for _f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"):
+    SAN_HOST_FLAGS += ["-Xarch_host", _f]
+SAN_LINK_FLAGS = ["-shared-libasan", "-fsanitize=address,undefined"]
+
+
+def san_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized builds link against."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return found[-1]
 
 
 def source_files() -> list[str]:
@@ -56,6 +75,29 @@ def _compile(src: str, obj: str, extra: list[str]) -> tuple[str, int, str]:
     cmd = [HIPCC] + COMPILE_FLAGS + extra + ["-c", "-o", obj, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     return " ".join(cmd), res.returncode, _filter(res.stderr)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """SAN_LIB: abi.hip with host sanitizers, the kernels as in the normal build."""
+    digest = source_hash()
+    objs = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES if s != "abi.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    extra = [f"-DFP8A_SOURCE_SHA256=\"{digest}\""] + SAN_HOST_FLAGS
+    san_obj = os.path.join(OBJDIR, "abi_san.o")
+    cmd, rc, err = _compile(os.path.join(CSRC, "abi.hip"), san_obj, extra)
+    if verbose:
+        print(cmd, flush=True)
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed ({rc}):\n{cmd}\n{err}")
+    cmd = [HIPCC] + LINK_FLAGS + SAN_LINK_FLAGS + ["-o", SAN_LIB + ".tmp", san_obj] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_filter(res.stderr)}")
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
 
 
 def build(verbose: bool = False) -> str:
@@ -88,4 +130,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose="-v" in sys.argv)
+    else:
+        build(verbose="-v" in sys.argv)
