@@ -76,7 +76,7 @@ typedef enum { FP8A_F32 = 0, FP8A_BF16 = 1, FP8A_F64 = 2, FP8A_E4M3 = 3, FP8A_I8
 #define FP8A_INT8_QK 16u
 
 typedef struct {
-  int32_t batch;     /* B >= 1; B * hq <= 65535 */
+  int32_t batch;     /* B >= 1; B * (hq + 2 hkv) <= 65535 */
   int32_t hq;        /* query heads >= 1 */
   int32_t hkv;       /* KV heads >= 1, hq % hkv == 0 */
   int32_t seqlen;    /* 1 <= N <= 2^30 (token count of every head) */

@@ -25,11 +25,12 @@ int check_shape(const fp8a_shape* s) {
   if (s->hq % s->hkv != 0) return FP8A_ERR_SHAPE;
   if (s->head_dim != 64 && s->head_dim != 128) return FP8A_ERR_SHAPE;
   if (s->seqlen > (1 << 30)) return FP8A_ERR_SHAPE;
-  // (batch, head) pairs index the prologue grids' second dimension (at most
-  // 65535 blocks), and the forward grid is one workgroup per (batch, query
-  // head, 128-token query tile), counted in 31 bits
+  // the prologue's max pass indexes (tensor, batch, head) by its grid's second
+  // dimension (at most 65535 blocks): B*hq query heads and B*hkv key and value
+  // heads each; the forward grid is one workgroup per (batch, query head,
+  // 128-token query tile), counted in 31 bits
   const int64_t bh = static_cast<int64_t>(s->batch) * s->hq;
-  if (bh > 65535) return FP8A_ERR_SHAPE;
+  if (static_cast<int64_t>(s->batch) * (s->hq + 2 * static_cast<int64_t>(s->hkv)) > 65535) return FP8A_ERR_SHAPE;
   if (bh * ((static_cast<int64_t>(s->seqlen) + 127) / 128) > INT32_MAX) return FP8A_ERR_SHAPE;
   return FP8A_OK;
 }

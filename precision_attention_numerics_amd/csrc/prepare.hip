@@ -42,9 +42,11 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float x[8]) {
   }
 }
 
-__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t value, int64_t n) {
+// Zeroes the scale maxima (n words) and, when given, the status word.
+__global__ void k_fill2_u32(uint32_t* __restrict__ p, int64_t n, uint32_t* __restrict__ status) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = value;
+  if (i < n) p[i] = 0u;
+  if (i == 0 && status) *status = 0u;
 }
 
 // Partial sums of the mean key: each group of D/8 lanes owns one chunk of 64
@@ -207,24 +209,36 @@ constexpr int kPrepThreads = 256;
 constexpr int kRowsPerBlock = 256;
 constexpr int kRowsInFlight = 4;
 
+// One tensor's share of a prologue pass: the rows of batch*head bh, block bx.
+struct RowsJob {
+  const void* x;
+  int64_t sb, sh, sn;     // element strides of (batch, head, token)
+  int32_t H;              // heads of this tensor
+  int32_t ntile;          // scale groups per head
+  uint32_t* amax;         // per head (ntile == 1) or per 128-token tile
+  float* desc;            // descales out (quantise pass)
+  uint8_t* codes;         // [B,H,Np,D] codes out (quantise pass)
+};
+
 // Max |x| of the transformed rows per head (ntile == 1) or per 128-token tile
-// of a head (amax[bh * ntile + tile]).  grid = (ceil(N / 256), B*H): a block's
-// rows are tiles 2*bx and 2*bx + 1.
+// of a head (amax[bh * ntile + tile]) for block (bx, bh): the block's rows are
+// tiles 2*bx and 2*bx + 1.
 template <typename IT, int D, bool ROT, bool CENTER>
-__global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
-                                                       int32_t H, int32_t N, const float* __restrict__ mu_all,
-                                                       int32_t hq_per_mu, const int8_t* __restrict__ signs,
-                                                       int32_t ntile, uint32_t* __restrict__ amax,
-                                                       int32_t* __restrict__ status) {
+__device__ __forceinline__ void amax_rows(const RowsJob& j, int bh, int bx, int32_t N, const float* __restrict__ mu_all,
+                                          const int8_t* __restrict__ signs, int32_t* __restrict__ status) {
   constexpr int L = D / 8;                 // lanes per row
   constexpr int RPI = kPrepThreads / L;    // rows per iteration
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const IT* __restrict__ x = static_cast<const IT*>(j.x);
+  const int64_t sb = j.sb, sh = j.sh, sn = j.sn;
+  const int32_t H = j.H, ntile = j.ntile;
+  uint32_t* __restrict__ amax = j.amax;
+  const int b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
-  const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
+  const float* mu = CENTER ? mu_all + static_cast<int64_t>(bh) * D : nullptr;
   const IT* base = x + b * sb + h * sh + 8 * li;
   float m = 0.0f, m_hi = 0.0f;   // rows [0, 128) and [128, 256) of the block
   bool bad = false;
-  const int n_begin = blockIdx.x * kRowsPerBlock;
+  const int n_begin = bx * kRowsPerBlock;
   // kRowsInFlight rows per lane group per step, loaded before any is
   // transformed.  Rows past N are not loaded and not counted; the L lanes of a
   // row share r, so the lane exchanges of a row always run on all its lanes.
@@ -278,10 +292,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_amax(const IT* __restrict__ x,
       if (half == 0) atomicMax(amax + bh, __float_as_uint(mm));
     } else if (n_begin + half * (kRowsPerBlock / 2) < N) {
       // each tile is written by exactly one block
-      atomicMax(amax + static_cast<int64_t>(bh) * ntile + 2 * blockIdx.x + half, __float_as_uint(mm));
+      atomicMax(amax + static_cast<int64_t>(bh) * ntile + 2 * bx + half, __float_as_uint(mm));
     }
     if (half == 0 && redbad && status) atomicOr(status, 1);
   }
+}
+
+// The max pass of Q, K and V in one launch: grid = (ceil(N / 256), B*hq +
+// 2*B*hkv); rows of blockIdx.y in [0, B*hq) are Q heads, then K heads
+// (centred with the mean key when CENTERK), then V heads (never transformed).
+template <typename IT, int D, bool ROT, bool CENTERK>
+__global__ __launch_bounds__(kPrepThreads) void k_amax_qkv(const RowsJob q, const RowsJob k, const RowsJob v,
+                                                           int32_t B, int32_t N, const float* __restrict__ mu,
+                                                           const int8_t* __restrict__ signs,
+                                                           int32_t* __restrict__ status) {
+  const int y = blockIdx.y, nq = B * q.H, nk = B * k.H;
+  if (y < nq) amax_rows<IT, D, ROT, false>(q, y, blockIdx.x, N, nullptr, signs, status);
+  else if (y < nq + nk) amax_rows<IT, D, ROT, CENTERK>(k, y - nq, blockIdx.x, N, mu, signs, status);
+  else amax_rows<IT, D, false, false>(v, y - nq - nk, blockIdx.x, N, nullptr, nullptr, status);
 }
 
 // Running maximum over each head's tile maxima (prefix scales), in place.
@@ -319,25 +347,25 @@ __device__ __forceinline__ void scales_from_amax(uint32_t abits, bool rotated, f
   if (rotated) desc = desc * cd;
 }
 
-// Quantise Q or K rows into [B,H,Np,D] codes; rows in [N, Np) are written as 0.
-// Scales per head (ntile == 1) or per 128-token tile (desc_out[bh * ntile + t]).
+// Quantise the Q or K rows of block (bx, bh) into [B,H,Np,D] codes; rows in
+// [N, Np) are written as 0.  Scales per head (ntile == 1) or per 128-token tile
+// (desc[bh * ntile + t]).
 template <typename IT, int D, bool ROT, bool CENTER>
-__global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restrict__ x, int64_t sb, int64_t sh, int64_t sn,
-                                                             int32_t H, int32_t N, int32_t Np, const float* __restrict__ mu_all,
-                                                             int32_t hq_per_mu, const int8_t* __restrict__ signs,
-                                                             int32_t ntile, const uint32_t* __restrict__ amax, float cd,
-                                                             int32_t int8, float* __restrict__ desc_out,
-                                                             uint8_t* __restrict__ codes) {
+__device__ __forceinline__ void quant_rows(const RowsJob& j, int bh, int bx, int32_t N, int32_t Np,
+                                           const float* __restrict__ mu_all, const int8_t* __restrict__ signs,
+                                           float cd, int32_t int8) {
   const float qmax = int8 ? 127.0f : 448.0f;
   constexpr int L = D / 8;
   constexpr int RPI = kPrepThreads / L;
-  // Blocks take heads and row ranges in the reverse of the max pass's order:
-  // the rows that pass read last are the likeliest still to sit in the
-  // memory-side cache, and they are read first here.
-  const int bx = gridDim.x - 1 - blockIdx.x;
-  const int bh = gridDim.y - 1 - blockIdx.y, b = bh / H, h = bh % H;
+  const IT* __restrict__ x = static_cast<const IT*>(j.x);
+  const int64_t sb = j.sb, sh = j.sh, sn = j.sn;
+  const int32_t H = j.H, ntile = j.ntile;
+  const uint32_t* __restrict__ amax = j.amax;
+  float* __restrict__ desc_out = j.desc;
+  uint8_t* __restrict__ codes = j.codes;
+  const int b = bh / H, h = bh % H;
   const int li = threadIdx.x % L, rl = threadIdx.x / L;
-  const float* mu = CENTER ? mu_all + static_cast<int64_t>(b * (H / hq_per_mu) + h / hq_per_mu) * D : nullptr;
+  const float* mu = CENTER ? mu_all + static_cast<int64_t>(bh) * D : nullptr;
   const int n_begin = bx * kRowsPerBlock;
   // scales of the block's rows [0, 128) and [128, 256)
   float inv, desc, inv_hi, desc_hi;
@@ -391,6 +419,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_rows(const IT* __restric
       if (n < Np) *reinterpret_cast<uint2*>(out + static_cast<int64_t>(n) * D) = w;
     }
   }
+}
+
+// The quantise pass of Q and K in one launch: grid = (ceil(Np / 256), B*hq +
+// B*hkv).  Blocks take row ranges and heads in the reverse of the max pass's
+// order (K before Q, last rows first): the rows that pass read last are the
+// likeliest still to sit in the memory-side cache.
+template <typename IT, int D, bool ROT, bool CENTERK>
+__global__ __launch_bounds__(kPrepThreads) void k_quant_qk(const RowsJob q, const RowsJob k, int32_t B, int32_t N,
+                                                           int32_t Np, const float* __restrict__ mu,
+                                                           const int8_t* __restrict__ signs, float cd, int32_t int8) {
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int y = gridDim.y - 1 - blockIdx.y, nq = B * q.H;
+  if (y < nq) quant_rows<IT, D, ROT, false>(q, y, bx, N, Np, nullptr, signs, cd, int8);
+  else quant_rows<IT, D, ROT, CENTERK>(k, y - nq, bx, N, Np, mu, signs, cd, int8);
 }
 
 // Quantise V (never rotated) into the transposed layout [B,Hkv,D,Np]: one block
@@ -453,28 +495,14 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
   const IT* v = static_cast<const IT*>(a.v);
   const int32_t nt = a.ntile;
   const int64_t n_amax = static_cast<int64_t>(B) * (hq * nt + hkv * nt + hkv);
-  k_fill_u32<<<dim3(static_cast<unsigned>((n_amax + 255) / 256)), blk, 0, st>>>(a.amax, 0u, n_amax);
-  if (a.status) k_fill_u32<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<uint32_t*>(a.status), 0u, 1);
+  k_fill2_u32<<<dim3(static_cast<unsigned>((n_amax + 255) / 256)), blk, 0, st>>>(
+      a.amax, n_amax, reinterpret_cast<uint32_t*>(a.status));
   uint32_t* amax_q = a.amax;
   uint32_t* amax_k = a.amax + static_cast<int64_t>(B) * hq * nt;
   uint32_t* amax_v = amax_k + static_cast<int64_t>(B) * hkv * nt;
-  const dim3 gq((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
-  const dim3 gk((N + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
-  const dim3 gq_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hq);
-  const dim3 gk_np((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * hkv);
   const float* mu = a.k_mean;
   const int i8 = a.int8 ? 1 : 0;
-  // Each tensor's passes run back to back (max, then quantise), so the
-  // quantise pass finds the rows the max pass read last still cached.
-  if (a.rotate) {
-    k_amax<IT, D, true, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, a.signs, nt, amax_q, a.status);
-    if (a.prefix) k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
-    k_quant_rows<IT, D, true, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, a.signs, nt, amax_q, a.cd, i8, a.q_desc, a.q8);
-  } else {
-    k_amax<IT, D, false, false><<<gq, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, nullptr, 1, nullptr, nt, amax_q, a.status);
-    if (a.prefix) k_prefix_max<<<dim3((B * hq + 255) / 256), blk, 0, st>>>(amax_q, B * hq, nt);
-    k_quant_rows<IT, D, false, false><<<gq_np, blk, 0, st>>>(q, a.qs[0], a.qs[1], a.qs[2], hq, N, Np, nullptr, 1, nullptr, nt, amax_q, a.cd, i8, a.q_desc, a.q8);
-  }
+  // mean key first: the K max pass subtracts it
   if (a.center) {
     constexpr int32_t kChunksPerBlock = 256 / (D / 8);
     k_kmean_partial<IT, D><<<dim3((a.np2 + kChunksPerBlock - 1) / kChunksPerBlock, B * hkv), dim3(256), 0, st>>>(
@@ -482,27 +510,32 @@ static hipError_t launch_prepare_t(const PrepareArgs& a, hipStream_t st) {
     k_kmean_final<<<dim3(B * hkv, D / kMeanCh), dim3(kMeanCh * kMeanW), 0, st>>>(a.mean_part, a.np2, a.n_mean, D,
                                                                                   a.k_mean);
   }
-  const int8_t* ks = a.rotate ? a.signs : nullptr;
+  const RowsJob jq{q, a.qs[0], a.qs[1], a.qs[2], hq, nt, amax_q, a.q_desc, a.q8};
+  const RowsJob jk{k, a.ks[0], a.ks[1], a.ks[2], hkv, nt, amax_k, a.k_desc, a.k8};
+  const RowsJob jv{v, a.vs[0], a.vs[1], a.vs[2], hkv, 1, amax_v, a.v_desc, a.v8t};
+  const dim3 g_max((N + kRowsPerBlock - 1) / kRowsPerBlock, B * (hq + 2 * hkv));
+  const dim3 g_quant((Np + kRowsPerBlock - 1) / kRowsPerBlock, B * (hq + hkv));
+  const int8_t* sg = a.rotate ? a.signs : nullptr;
   if (a.rotate && a.center) {
-    k_amax<IT, D, true, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, ks, nt, amax_k, a.status);
+    k_amax_qkv<IT, D, true, true><<<g_max, blk, 0, st>>>(jq, jk, jv, B, N, mu, sg, a.status);
   } else if (a.rotate) {
-    k_amax<IT, D, true, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, ks, nt, amax_k, a.status);
+    k_amax_qkv<IT, D, true, false><<<g_max, blk, 0, st>>>(jq, jk, jv, B, N, mu, sg, a.status);
   } else if (a.center) {
-    k_amax<IT, D, false, true><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, mu, 1, nullptr, nt, amax_k, a.status);
+    k_amax_qkv<IT, D, false, true><<<g_max, blk, 0, st>>>(jq, jk, jv, B, N, mu, sg, a.status);
   } else {
-    k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, nullptr, 1, nullptr, nt, amax_k, a.status);
+    k_amax_qkv<IT, D, false, false><<<g_max, blk, 0, st>>>(jq, jk, jv, B, N, mu, sg, a.status);
   }
-  if (a.prefix) k_prefix_max<<<dim3((B * hkv + 255) / 256), blk, 0, st>>>(amax_k, B * hkv, nt);
+  // Q and K tile maxima are contiguous: one running-max launch covers both
+  if (a.prefix) k_prefix_max<<<dim3((B * (hq + hkv) + 255) / 256), blk, 0, st>>>(amax_q, B * (hq + hkv), nt);
   if (a.rotate && a.center) {
-    k_quant_rows<IT, D, true, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, ks, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+    k_quant_qk<IT, D, true, true><<<g_quant, blk, 0, st>>>(jq, jk, B, N, Np, mu, sg, a.cd, i8);
   } else if (a.rotate) {
-    k_quant_rows<IT, D, true, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, ks, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+    k_quant_qk<IT, D, true, false><<<g_quant, blk, 0, st>>>(jq, jk, B, N, Np, mu, sg, a.cd, i8);
   } else if (a.center) {
-    k_quant_rows<IT, D, false, true><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, mu, 1, nullptr, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+    k_quant_qk<IT, D, false, true><<<g_quant, blk, 0, st>>>(jq, jk, B, N, Np, mu, sg, a.cd, i8);
   } else {
-    k_quant_rows<IT, D, false, false><<<gk_np, blk, 0, st>>>(k, a.ks[0], a.ks[1], a.ks[2], hkv, N, Np, nullptr, 1, nullptr, nt, amax_k, a.cd, i8, a.k_desc, a.k8);
+    k_quant_qk<IT, D, false, false><<<g_quant, blk, 0, st>>>(jq, jk, B, N, Np, mu, sg, a.cd, i8);
   }
-  k_amax<IT, D, false, false><<<gk, blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, nullptr, 1, nullptr, 1, amax_v, a.status);
   k_quant_vt<IT, D><<<dim3(Np / 128, B * hkv), blk, 0, st>>>(v, a.vs[0], a.vs[1], a.vs[2], hkv, N, Np, amax_v, a.v_desc, a.v8t);
   (void)grp;
   return hipGetLastError();

@@ -102,6 +102,8 @@ def test_prepare_rejects(abi):
     assert _prep(abi, abi.make_shape(1, 2, 1, 0, 64)) == -2           # seqlen
     assert _prep(abi, abi.make_shape(1, 2, 1, (1 << 30) + 1, 64)) == -2   # seqlen above 2^30
     assert _prep(abi, abi.make_shape(32768, 2, 1, 64, 64)) == -2      # batch * hq above the grid limit
+    assert _prep(abi, abi.make_shape(21845, 3, 3, 64, 64)) == -2      # batch * (hq + 2 hkv) above it
+    assert _prep(abi, abi.make_shape(7281, 3, 3, 64, 64), ws_bytes=1) == -5   # 65529 heads in all: accepted
     assert _prep(abi, abi.make_shape(4096, 8, 1, 1 << 30, 64)) == -2  # forward grid beyond 31 bits
     assert _prep(abi, ok, dtype=2) == -3                               # f64 input
     assert _prep(abi, ok, flags=32) == -4                              # unknown flag
