@@ -87,9 +87,8 @@ def profiled_traffic(kernel: str, summary: str = "attn_fwd_long_context_32k.json
 
 def kernel_name(args) -> str:
     """The forward kernel the timed launch runs (as rocprofv3 names it)."""
-    if args.int8_qk:
-        return "k_attn_fwd<128, 128, 2, true, true, false, false, true>"
-    return "k_attn_fwd_pipe<true, true, %s, 2>" % ("true" if args.tile_scales else "false")
+    return "k_attn_fwd_pipe<true, true, %s, 2, %s>" % ("true" if args.tile_scales else "false",
+                                                       "true" if args.int8_qk else "false")
 
 
 def sample_rows(N: int, tiles: int) -> np.ndarray:

@@ -20,7 +20,6 @@ struct FwdParams {
   int32_t B, hq, hkv, N, Np, n_qtiles, kv_order, k_sink;
   int32_t tiles;          // 1: q_desc [B*hq*n_qtiles], k_desc [B*hkv*n_qtiles] per 128-token tile
   int32_t int8;           // 1: q8 / k8 hold int8 codes (exact integer scores)
-  int32_t no_pipe;        // 1: use the unpipelined kernel even where the pipelined one applies
   float ls2;              // RN32(softmax_scale * log2 e)
   float S;                // static P scale
   float inv_S;            // 1/S when S is a power of two

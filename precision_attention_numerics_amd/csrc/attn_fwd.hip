@@ -614,6 +614,37 @@ __device__ __forceinline__ void init_tile(Tile& X, const uint8_t* q8, int bh, in
   for (int ct = 0; ct < D / 16; ++ct) X.o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// S^T of key tile t (operand a, read from LDS) for the NT query tiles of the
+// wave.  E4M3 codes: one 16x16x128 instruction per query tile.  Int8 codes:
+// two 16x16x64 instructions; each operand's 32 channels per lane (channels
+// [32 lg, 32 lg + 32)) are split into the same two 16-byte halves on both
+// sides, so the pair sums every channel once, and the int32 sum is exact
+// (|s| <= 127^2 * 128 < 2^24).  It is kept as its bit pattern in s until the
+// softmax front converts it (front_step, I8).
+template <bool I8, int NT>
+__device__ __forceinline__ void qk_tiles(const v8i a, Tile (&X)[NT], int t) {
+  if constexpr (I8) {
+    const v4i alo = v4i{a[0], a[1], a[2], a[3]}, ahi = v4i{a[4], a[5], a[6], a[7]};
+    v4i acc[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) acc[k] = mfma_i8(alo, v4i{X[k].q[0], X[k].q[1], X[k].q[2], X[k].q[3]}, v4i{0, 0, 0, 0});
+#pragma unroll
+    for (int k = 0; k < NT; ++k) acc[k] = mfma_i8(ahi, v4i{X[k].q[4], X[k].q[5], X[k].q[6], X[k].q[7]}, acc[k]);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) X[k].s[t] = __builtin_bit_cast(v4f, acc[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) X[k].s[t] = mfma_f8(a, X[k].q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+  }
+}
+
+// Int8 scores of key tile t, held as int32 bit patterns, to binary32 (exact).
+__device__ __attribute__((always_inline)) inline void scores_to_f32(Tile& X, int t) {
+  const v4i v = __builtin_bit_cast(v4i, X.s[t]);
+  X.s[t] = v4f{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+               static_cast<float>(v[3])};
+}
+
 // Epilogue of one tile: out = acc * (v_desc / (S * l)); the lane holds
 // channels 16 ct + 4 lg + r of its query row.
 __device__ __forceinline__ void store_tile(const Tile& X, const FwdParams& p, int bh, int N, float vdesc, int lg) {
@@ -671,9 +702,26 @@ struct Front {
 // FIRST: the first block visited.  Every row has a visible key in it (the
 // diagonal block holds key 128*qtile, block 0 holds key 0), so after it the
 // running max is finite and the -inf cases of mc and alpha cannot occur.
-template <int K, bool MASK, bool CAUSAL, bool TILES, bool FIRST = true>
+// I8: the scores arrive as int32 bit patterns and are converted chunk by chunk
+// before the max reads them (all at once where the block is masked).
+template <int K, bool MASK, bool CAUSAL, bool TILES, bool FIRST = true, bool I8 = false>
 __device__ __attribute__((always_inline)) inline void front_step(Front& f, Tile& X, const float c, const int jb,
                                                                  const int N, const FwdParams& p) {
+  if constexpr (I8) {
+    if constexpr (K == 0) {
+      constexpr int last = MASK ? T : 3;
+#pragma unroll
+      for (int t = 0; t < last; ++t) scores_to_f32(X, t);
+    } else if constexpr (!MASK && K == 1) {
+      scores_to_f32(X, 3);
+      scores_to_f32(X, 4);
+    } else if constexpr (!MASK && K == 2) {
+      scores_to_f32(X, 5);
+      scores_to_f32(X, 6);
+    } else if constexpr (!MASK && K == 3) {
+      scores_to_f32(X, 7);
+    }
+  }
   if constexpr (K == 0) {
     if constexpr (MASK) {
       const int lim = min(N, CAUSAL ? X.i + 1 : N) - jb;
@@ -813,7 +861,9 @@ __device__ __attribute__((always_inline)) inline void back_step(float (&part)[T]
 // registers each) and each K/V operand read from LDS feeds two matrix
 // instructions; with NT = 1 four waves share a SIMD (128 registers each), so
 // more waves interleave their vector work, for twice the LDS reads per row.
-template <bool CAUSAL, bool POW2, bool TILES, int NT>
+// I8: Q and K hold int8 codes (exact integer scores on the 16x16x64 int8
+// instruction, qk_tiles); P and V stay E4M3.
+template <bool CAUSAL, bool POW2, bool TILES, int NT, bool I8>
 __global__ __launch_bounds__(64 * 8 / NT, 4 / NT) void k_attn_fwd_pipe(const FwdParams p) {
   using namespace pipe;
   constexpr int W = 8 / NT;
@@ -883,7 +933,7 @@ __global__ __launch_bounds__(64 * 8 / NT, 4 / NT) void k_attn_fwd_pipe(const Fwd
     const float c = c_of(blk);
     const int jb = blk * BC + KPL * lg;
     static_for<0, T>([&](auto kc) __attribute__((always_inline)) {
-      front_step<decltype(kc)::value, M, CAUSAL, TILES>(f, X, c, jb, N, p);
+      front_step<decltype(kc)::value, M, CAUSAL, TILES, true, I8>(f, X, c, jb, N, p);
     });
     X.alpha = f.alpha;
     if (f.gate) softmax_screen<T>(X.s, p);
@@ -915,9 +965,7 @@ __global__ __launch_bounds__(64 * 8 / NT, 4 / NT) void k_attn_fwd_pipe(const Fwd
   fill_v<W>(vrs, blk_of(0), wv, voff, vlds);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const v8i a = lds_read_pair(klds + kofs0 + t * 256 * UK, klds + kofs1 + t * 256 * UK);
-#pragma unroll
-    for (int k = 0; k < NT; ++k) X[k].s[t] = mfma_f8(a, X[k].q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    qk_tiles<I8>(lds_read_pair(klds + kofs0 + t * 256 * UK, klds + kofs1 + t * 256 * UK), X, t);
   }
   front_first(blk_of(0));
 
@@ -966,13 +1014,12 @@ __global__ __launch_bounds__(64 * 8 / NT, 4 / NT) void k_attn_fwd_pipe(const Fwd
       if constexpr (n < 8) {
 #pragma unroll
         for (int k = 0; k < NT; ++k) back_step<j, MB, POW2>(part[k], X[k], p);
-#pragma unroll
-        for (int k = 0; k < NT; ++k) X[k].s[j] = mfma_f8(ops[n % 3], X[k].q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        qk_tiles<I8>(ops[n % 3], X, j);
       } else {
 #pragma unroll
         for (int k = 0; k < NT; ++k) X[k].o[j] = mfma_f8(ops[n % 3], X[k].pop, X[k].o[j]);
 #pragma unroll
-        for (int k = 0; k < NT; ++k) front_step<j, MF, CAUSAL, TILES, false>(f[k], X[k], cn, jbn, N, p);
+        for (int k = 0; k < NT; ++k) front_step<j, MF, CAUSAL, TILES, false, I8>(f[k], X[k], cn, jbn, N, p);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1103,12 +1150,12 @@ template <int D, int BC, bool CAUSAL, bool POW2, bool DUMP>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.B * p.hq * p.n_qtiles));
   if constexpr (D == 128 && BC == 128 && !DUMP) {
-    if (!p.int8 && !p.no_pipe) {
-      constexpr int NT = kPipeTiles;
-      if (p.tiles) k_attn_fwd_pipe<CAUSAL, POW2, true, NT><<<grid, dim3(64 * 8 / NT), 0, st>>>(p);
-      else k_attn_fwd_pipe<CAUSAL, POW2, false, NT><<<grid, dim3(64 * 8 / NT), 0, st>>>(p);
-      return hipGetLastError();
-    }
+    constexpr int NT = kPipeTiles;
+    const dim3 block(64 * 8 / NT);
+    if (p.int8) k_attn_fwd_pipe<CAUSAL, POW2, false, NT, true><<<grid, block, 0, st>>>(p);
+    else if (p.tiles) k_attn_fwd_pipe<CAUSAL, POW2, true, NT, false><<<grid, block, 0, st>>>(p);
+    else k_attn_fwd_pipe<CAUSAL, POW2, false, NT, false><<<grid, block, 0, st>>>(p);
+    return hipGetLastError();
   }
   if (p.tiles) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, true, false><<<grid, dim3(kThreads), 0, st>>>(p);
   else if (p.int8) k_attn_fwd<D, BC, 2, CAUSAL, POW2, DUMP, false, true><<<grid, dim3(kThreads), 0, st>>>(p);
