@@ -21,8 +21,8 @@ import csv
 import os
 import sys
 
-KERNELS = ("k_attn_fwd", "k_attn_pcast", "k_amax", "k_prefix_max", "k_quant_qk", "k_quant_vt", "k_kmean_partial",
-           "k_kmean_final", "k_head_err_partial", "k_head_err_final", "k_fill2_u32")
+KERNELS = ("k_attn_fwd", "k_attn_pcast", "k_amax", "k_prefix_max", "k_quant_qk", "k_quant_vt",
+           "k_kmean_partial", "k_kmean_final", "k_head_err_partial", "k_head_err_final", "k_fill2_u32")
 COPY_BYTES = 1024 * (1 << 20)
 
 
