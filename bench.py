@@ -85,6 +85,15 @@ def profiled_traffic(kernel: str, summary: str = "attn_fwd_long_context_32k.json
     return None
 
 
+def provenance(torch, pan) -> dict:
+    """What the line was measured on: the device, and the build of the
+    library that ran (the hash of the sources it was built from)."""
+    props = torch.cuda.get_device_properties(0)
+    return {"device": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count, "library_build": pan._abi.build_info(),
+            "torch": torch.__version__, "hip": torch.version.hip}
+
+
 def kernel_name(args) -> str:
     """The forward kernel the timed launch runs (as rocprofv3 names it)."""
     return "k_attn_fwd_pipe<true, true, %s, 2, %s>" % ("true" if args.tile_scales else "false",
@@ -293,6 +302,7 @@ def main():
                      "flop_per_launch": flop},
         "cpu_baseline": cpu,
         "detail": results,
+        "provenance": provenance(torch, pan),
     }
     print(json.dumps(line), flush=True)
 

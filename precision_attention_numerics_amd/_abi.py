@@ -65,6 +65,8 @@ def _load():
     lib.fp8_attn_head_error.restype = ctypes.c_int
     lib.fp8_attn_strerror.argtypes = [ctypes.c_int]
     lib.fp8_attn_strerror.restype = ctypes.c_char_p
+    lib.fp8_attn_build_info.argtypes = []
+    lib.fp8_attn_build_info.restype = ctypes.c_char_p
     return lib
 
 
@@ -79,6 +81,11 @@ def header_functions() -> list[str]:
 
 def strerror(status: int) -> str:
     return _lib.fp8_attn_strerror(int(status)).decode()
+
+
+def build_info() -> str:
+    """The loaded library's build identifier ("source_sha256=<hex> arch=gfx950")."""
+    return _lib.fp8_attn_build_info().decode()
 
 
 def _ptr(t: torch.Tensor | None):
