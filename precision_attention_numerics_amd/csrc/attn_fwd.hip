@@ -574,20 +574,6 @@ __device__ __forceinline__ void fill_v(const __amdgpu_buffer_rsrc_t vrs, int blk
                                              0);
 }
 
-// S^T of one query tile for the block in kt: eight 16-key MFMA tiles.
-__device__ __forceinline__ void qk(const uint8_t* kt, int kofs0, int kofs1, v8i q, v4f (&s)[T]) {
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-    s[t] = mfma_f8(lds_read_pair(kt + kofs0 + t * 256 * UK, kt + kofs1 + t * 256 * UK), q, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-}
-
-// O^T += V^T P^T of one query tile for the block in vt.
-__device__ __forceinline__ void pv(const uint8_t* vt, int vofs0, int vofs1, v8i pop, v4f (&o)[D / 16]) {
-#pragma unroll
-  for (int ct = 0; ct < D / 16; ++ct)
-    o[ct] = mfma_f8(lds_read_pair(vt + vofs0 + ct * 256 * UV, vt + vofs1 + ct * 256 * UV), pop, o[ct]);
-}
-
 // Per-tile running state.
 struct Tile {
   v8i q;            // Q operand (B of S^T = K Q^T)
