@@ -8,15 +8,23 @@
 //
 // Mapping onto CDNA4:
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//    owns QT tiles of 16 rows.  K (row-major) and V (transposed, token axis
-//    contiguous) tiles of BC keys are staged in LDS; the next tile is
-//    prefetched into registers while the current one is consumed.
+//    owns two tiles of 16 rows.  K (row-major) and V (transposed, token axis
+//    contiguous) tiles of BC keys are staged in LDS by buffer-to-LDS DMA into
+//    double buffers, the next block's tiles in flight while the current ones
+//    are read.
 //  * S^T = K Q^T with v_mfma_f32_16x16x128_f8f6f4 (the whole head_dim = 128 in
-//    one instruction; head_dim 64 is zero-padded).  The K rows of key tile t
-//    are permuted so that accumulator lane group g ends up holding keys
+//    one instruction; head_dim 64 is zero-padded here); int8 Q/K codes use two
+//    16x16x64 int8 instructions per key tile.  The K rows of key tile t are
+//    permuted so that accumulator lane group g ends up holding keys
 //    [g*BC/4, (g+1)*BC/4) of the block for its query: those bytes, once cast,
 //    are exactly the B operand of the P.V instruction (O^T = V^T P^T), so P
 //    never goes through LDS.
+//  * k_attn_fwd_pipe (head_dim 128, blocks of 128: the timed forward) runs the
+//    same per-tile arithmetic as k_attn_fwd in a software pipeline across
+//    blocks: each step issues Q.K^T of the next block between the chunks of
+//    this block's exp/cast half, then P.V of this block between the chunks of
+//    the next block's max/fma half.  k_attn_fwd, block by block, serves the
+//    P~ dump, row checksum and underflow-count forms and blocks of 64.
 //  * Workgroups are ordered longest-first (causal) and grouped by head per XCD
 //    so the K/V of a head stay in one XCD's L2.
 #include <type_traits>
